@@ -1,0 +1,214 @@
+"""ctypes binding of libsdv (include/sdv.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the path runs in the library's kernels.
+The functions carry the C names.  A missing library is an error, never a
+fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdv.so")
+_lib = None
+
+SD_OK = 0
+SD_EINVAL = -1
+SD_ERANGE = -2
+SD_EUNSUPPORTED = -3
+SD_ELAUNCH = -4
+
+SD_DTYPE_F32 = 0
+SD_DTYPE_BF16 = 1
+
+SD_SCHED_EARLY_STOP = 0
+SD_SCHED_GLOBAL_ARGMAX = 1
+SD_SCHED_CAPPED_TOPK = 2
+
+SD_ST_BAD_TOKEN = 1
+SD_ST_NONFINITE = 2
+SD_ST_ZERO_Z = 4
+SD_ST_ZERO_RESIDUAL = 8
+SD_ST_ZERO_Q = 16
+
+EXPORTS = (
+    "sd_abi_version", "sd_status_string", "sd_schedule", "sd_verify_workspace_size",
+    "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
+)
+
+
+class SdvError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {code} ({status_string(code)})")
+        self.code = code
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+
+
+def lib():
+    """Load libsdv.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.sd_abi_version.restype = _I
+    L.sd_abi_version.argtypes = []
+    L.sd_status_string.restype = ctypes.c_char_p
+    L.sd_status_string.argtypes = [_I]
+    L.sd_schedule.restype = _I
+    L.sd_schedule.argtypes = [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
+    L.sd_verify_workspace_size.restype = _SZ
+    L.sd_verify_workspace_size.argtypes = [_I, _I, _I]
+    L.sd_verify.restype = _I
+    L.sd_verify.argtypes = [_P, _I, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P, _P,
+                            _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+    L.sd_markov_draft_workspace_size.restype = _SZ
+    L.sd_markov_draft_workspace_size.argtypes = [_I, _I, _I, _I]
+    L.sd_markov_draft.restype = _I
+    L.sd_markov_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P,
+                                  _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
+    _lib = L
+    return L
+
+
+def sd_abi_version():
+    return lib().sd_abi_version()
+
+
+def status_string(code):
+    return lib().sd_status_string(int(code)).decode()
+
+
+sd_status_string = status_string
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn, code):
+    if code != SD_OK:
+        raise SdvError(fn, code)
+
+
+def _workspace(nbytes, device):
+    # 256-byte aligned by torch's caching allocator
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, stream=None):
+    """Run the scheduler.  conf [R][gmax] fp32, sps fp32, gamma_r [R] int32 or
+    None, cap_k a 1-element int32 device tensor (CAPPED_TOPK).  Returns a dict
+    of device tensors: ell, batch, n_sel, theta, surv."""
+    R, gmax = conf.shape
+    dev = conf.device
+    o = out or {}
+    ell = o.get("ell", torch.empty(R, dtype=torch.int32, device=dev))
+    batch = o.get("batch", torch.empty(1, dtype=torch.int32, device=dev))
+    n_sel = o.get("n_sel", torch.empty(1, dtype=torch.int32, device=dev))
+    theta = o.get("theta", torch.empty(1, dtype=torch.float64, device=dev))
+    sv = o.get("surv", torch.empty((R, gmax), dtype=torch.float32, device=dev)) if surv else None
+    code = lib().sd_schedule(
+        _stream(stream), R, gmax, _ptr(gamma_r, torch.int32, "gamma_r"),
+        _ptr(conf, torch.float32, "conf"), _ptr(sps, torch.float32, "sps"), sps.numel(), int(mode),
+        _ptr(cap_k, torch.int32, "cap_k"), _ptr(ell, torch.int32), _ptr(batch, torch.int32),
+        _ptr(n_sel, torch.int32), _ptr(theta, torch.float64), _ptr(sv, torch.float32))
+    _check("sd_schedule", code)
+    return dict(ell=ell, batch=batch, n_sel=n_sel, theta=theta, surv=sv)
+
+
+def sd_verify_workspace_size(R, gmax, V):
+    return lib().sd_verify_workspace_size(R, gmax, V)
+
+
+def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.0, seed=0,
+              pos0=None, probe=False, stats=False, workspace=None, out=None, stream=None,
+              prof_events=None):
+    """Run verification.  tgt / drf: 2-D logit tensors (bf16 or fp32, ld =
+    shape[1]); the rest int32 device tensors.  Returns a dict of device
+    tensors: n_acc, tokens, status (and probe, row_stats if asked).
+    prof_events: optional pair of raw hipEvent_t handles (ints) recorded
+    around the row-statistics pass."""
+    R, gmax = draft_tokens.shape
+    dev = tgt.device
+    if tgt.dtype == torch.bfloat16:
+        dt = SD_DTYPE_BF16
+    elif tgt.dtype == torch.float32:
+        dt = SD_DTYPE_F32
+    else:
+        raise TypeError("logits must be bf16 or fp32")
+    if drf.dtype != tgt.dtype or drf.shape[1] != tgt.shape[1]:
+        raise ValueError("target and draft rows must share dtype and leading dimension")
+    ld = tgt.shape[1]
+    o = out or {}
+    n_acc = o.get("n_acc", torch.empty(R, dtype=torch.int32, device=dev))
+    toks = o.get("tokens", torch.empty((R, gmax + 1), dtype=torch.int32, device=dev))
+    status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
+    pp = o.get("probe", torch.zeros((R, gmax, 2), dtype=torch.float32, device=dev)) if probe else None
+    rs = o.get("row_stats", torch.zeros((R, 2 * gmax + 1, 2), dtype=torch.float32, device=dev)) if stats else None
+    wsz = sd_verify_workspace_size(R, gmax, V)
+    ws = workspace if workspace is not None else _workspace(wsz, dev)
+    code = lib().sd_verify(
+        _stream(stream), R, gmax, int(V), ld, dt, float(temperature), int(seed) & (2**64 - 1),
+        _ptr(pos0, torch.int64, "pos0"), _ptr(tgt, None, "tgt"), _ptr(tgt_row0, torch.int32, "tgt_row0"),
+        _ptr(drf, None, "drf"), _ptr(drf_row0, torch.int32, "drf_row0"),
+        _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(ell, torch.int32, "ell"),
+        _ptr(n_acc, torch.int32), _ptr(toks, torch.int32), _ptr(status, torch.int32),
+        _ptr(pp, torch.float32), _ptr(rs, torch.float32), ws.data_ptr(), ws.numel(),
+        *(prof_events if prof_events else (None, None)))
+    _check("sd_verify", code)
+    return dict(n_acc=n_acc, tokens=toks, status=status, probe=pp, row_stats=rs)
+
+
+def sd_markov_draft_workspace_size(R, gamma, V, rank):
+    return lib().sd_markov_draft_workspace_size(R, gamma, V, rank)
+
+
+def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, workspace=None,
+                    out=None, stream=None):
+    """Run the Markov drafting head.  Returns a dict of device tensors:
+    tokens [R][gamma], q_logits [R][gamma][V] bf16, conf [R][gamma], status [R]."""
+    R, gamma, V = U.shape
+    rank = A.shape[2]
+    H = h.shape[2]
+    rank_e = E.shape[1]
+    dev = U.device
+    bf = torch.bfloat16
+    o = out or {}
+    tokens = o.get("tokens", torch.empty((R, gamma), dtype=torch.int32, device=dev))
+    ql = o.get("q_logits", torch.empty((R, gamma, V), dtype=bf, device=dev))
+    conf = o.get("conf", torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
+    wsz = sd_markov_draft_workspace_size(R, gamma, V, rank)
+    ws = workspace if workspace is not None else _workspace(wsz, dev)
+    code = lib().sd_markov_draft(
+        _stream(stream), R, gamma, V, rank, float(temperature), int(seed) & (2**64 - 1),
+        _ptr(pos0, torch.int64, "pos0"), _ptr(U, bf, "U"), _ptr(A, bf, "A"), _ptr(Ct, bf, "Ct"),
+        _ptr(x0, torch.int32, "x0"), _ptr(h, bf, "h"), H, _ptr(E, bf, "E"), rank_e,
+        _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf), _ptr(conf, torch.float32),
+        _ptr(status, torch.int32), ws.data_ptr(), ws.numel())
+    _check("sd_markov_draft", code)
+    return dict(tokens=tokens, q_logits=ql, conf=conf, status=status)

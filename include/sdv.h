@@ -1,0 +1,232 @@
+/*
+ * sdv.h - C ABI of libsdv: the per-step hot path of confidence-scheduled
+ * speculative decoding on one MI355X (gfx950) GPU.
+ *
+ * Three operations, each asynchronous on a caller-given HIP stream:
+ *
+ *   sd_schedule      survival products, candidate sort and the greedy
+ *                    Theta = tau * SPS(B) verify-batch selection
+ *   sd_verify        lossless rejection sampling over full vocabulary rows
+ *   sd_markov_draft  the low-rank Markov drafting head and the confidence head
+ *
+ * Sources, by page and section:
+ *   [DS]  "DSpark: Confidence-Scheduled Speculative Decoding with
+ *         Semi-Autoregressive Generation" (paper summary page):
+ *         "innovation one" (parallel backbone + Markov head), "2.1 confidence
+ *         head", "2.2 hardware-aware prefix scheduler", Figure 1,
+ *         "challenge 2: async scheduling and ZOS compatibility".
+ *   [SD]  speculative-decoding history page: "1.1 mechanism" (parallel
+ *         verification, rejection sampling, discard after the first
+ *         rejection, losslessness); DSpark "move one" (Markov head,
+ *         low-rank V x V table), "move two" (survival products), "move three"
+ *         (greedy scheduler against a throughput curve).
+ *   [LS]  LightSpec article, system section: token slots reserved at the
+ *         maximum draft length and cut after the fact (the padded row layout).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     stated otherwise.  The library never allocates, frees or synchronises;
+ *     all scratch lives in a caller-provided workspace of at least
+ *     sd_*_workspace_size() bytes (256-byte aligned).
+ *   - The return value reports host-side argument checks and launch errors
+ *     only (SD_OK or a negative SD_E* code).  Nothing is enqueued when an
+ *     argument check fails.  Data-dependent faults are reported per request
+ *     in a device status array (SD_ST_* bits) with the defined fallbacks
+ *     given at each function.
+ *   - Random decisions use a counter hash, never device state: SplitMix64
+ *     (Steele, Lea, Flood 2014) nested as
+ *         h = sm(sm(sm(sm(seed) ^ r) ^ pos) ^ draw),  sm(x) = mix(x + 0x9e3779b97f4a7c15)
+ *         u = (h >> 40) * 2^-24
+ *     with r the request index, pos = pos0[r] + (1-based draft position) and
+ *     draw 0 = draft sample, 1 = accept test, 2 = correction sample.  Calls
+ *     are therefore deterministic and replayable for given (seed, pos0).
+ *   - Logit rows are row-major with a leading dimension ld (elements, a
+ *     multiple of 8 so that every row starts 16-byte aligned); only the first
+ *     V entries of a row are read.  V must be a multiple of 8.
+ *   - bf16 data is passed as raw 16-bit patterns (uint16_t).
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDV_ABI_VERSION 1
+
+/* return codes (host side) */
+#define SD_OK             0
+#define SD_EINVAL        -1   /* bad size, null required pointer, bad mode / dtype / temperature */
+#define SD_ERANGE        -2   /* a table or workspace too small for the sizes given */
+#define SD_EUNSUPPORTED  -3   /* sizes beyond this build's limits */
+#define SD_ELAUNCH       -4   /* the HIP runtime refused a launch */
+
+/* logit dtypes */
+#define SD_DTYPE_F32   0
+#define SD_DTYPE_BF16  1
+
+/* scheduler modes [DS 2.2, challenge 2] */
+#define SD_SCHED_EARLY_STOP     0
+#define SD_SCHED_GLOBAL_ARGMAX  1
+#define SD_SCHED_CAPPED_TOPK    2
+
+/* per-request device status bits */
+#define SD_ST_BAD_TOKEN      1   /* token id outside [0, V) */
+#define SD_ST_NONFINITE      2   /* a needed logit row holds NaN or +inf */
+#define SD_ST_ZERO_Z         4   /* a needed logit row is entirely -inf */
+#define SD_ST_ZERO_RESIDUAL  8   /* rejection with no residual mass: drawn from p */
+#define SD_ST_ZERO_Q        16   /* q(x) = 0 at a tested draft token */
+
+/* build limits */
+#define SD_MAX_GAMMA           255     /* draft positions per request */
+#define SD_MAX_SCHED_SLOTS     16384   /* R * gamma_max for sd_schedule */
+#define SD_MAX_VOCAB           (1 << 24)
+
+/* ABI version of the loaded library (SDV_ABI_VERSION at build time). */
+int sd_abi_version(void);
+
+/* Static text for a return code or for one SD_ST_* bit; never NULL. */
+const char* sd_status_string(int code);
+
+/*
+ * sd_schedule - hardware-aware prefix scheduler [DS 2.2; SD move two/three].
+ *
+ * Survival a[r][j] = prod_{i<=j} conf[r][i] (fp32, left to right) is the
+ * chance that request r's draft prefix up to position j is accepted.  All
+ * candidates (r, j), j = 1..gamma_r[r], are ordered by survival descending,
+ * ties by r then j ascending; since a is non-increasing in j every prefix of
+ * this order is prefix-closed per request.  tau_n, the expected accepted
+ * tokens of the first n candidates, is summed in fixed point
+ * (q = rint(a * 2^32), integer prefix sums, tau_n = T_n * 2^-32, exact) and
+ *   Theta_n = tau_n * sps[R + n - 1]   (fp64; Theta_0 = 0)
+ * where sps[B-1] is the verification throughput at batch B = R + n.
+ *   mode EARLY_STOP:    n* = (first n >= 1 with Theta_n < Theta_{n-1}) - 1,
+ *                       else N  [DS 2.2 "stop once throughput falls"]
+ *   mode GLOBAL_ARGMAX: n* = smallest n maximising Theta_n over n = 0..N
+ *   mode CAPPED_TOPK:   n* = min(max(*cap_k, 0), N): the capacity was fixed
+ *                       before these confidences were known [DS challenge 2];
+ *                       pass a previous GLOBAL_ARGMAX call's n_sel pointer as
+ *                       cap_k to chain the two without a host round trip.
+ * Then ell[r] = number of selected candidates of request r, batch = R + n*.
+ *
+ *   R          requests, >= 0;   gamma_max in [0, SD_MAX_GAMMA];
+ *              R * gamma_max <= SD_MAX_SCHED_SLOTS
+ *   gamma_r    [R] int32 drafted length per request, clamped to
+ *              [0, gamma_max]; NULL means gamma_max for all
+ *   conf       [R][gamma_max] fp32 confidences in [0, 1] (finite)
+ *   sps        [sps_len] fp32 throughput table, sps[B-1] for batch B;
+ *              sps_len >= R * (1 + gamma_max) else SD_ERANGE
+ *   cap_k      [1] int32, read in CAPPED_TOPK mode only (device)
+ *   ell        [R] int32 out
+ *   batch, n_sel  [1] int32 out or NULL;  theta [1] fp64 out (Theta_{n*}) or NULL
+ *   surv       [R][gamma_max] fp32 out or NULL: a[r][j-1], 0 past gamma_r
+ * Runs as one workgroup; nothing is read back to the host.
+ */
+int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r,
+                const float* conf, const float* sps, int sps_len, int mode,
+                const int32_t* cap_k, int32_t* ell, int32_t* batch, int32_t* n_sel,
+                double* theta, float* surv);
+
+/*
+ * sd_verify - lossless verification by rejection sampling [SD 1.1].
+ *
+ * Request r drafted x_j = draft_tokens[r][j-1], j = 1..ell[r].  Its target
+ * row for position j (the row that scores x_j) is tgt_row0[r] + j - 1, for
+ * j = 1..ell[r]+1; its draft row for position j is drf_row0[r] + j - 1.
+ * (The padded layout of [LS] is tgt_row0[r] = r * (gamma_max + 1),
+ * drf_row0[r] = r * gamma_max; a packed layout works as well.)
+ * With p_j = softmax(target row / T) and q_j = softmax(draft row / T):
+ *   accept x_j iff u(r, pos0[r]+j, 1) * q_j(x_j) < p_j(x_j), i.e. with
+ *   probability min(1, p/q); stop at the first rejection j*;
+ *   on rejection draw the replacement from max(0, p_j* - q_j*) normalised
+ *   (the law that makes the output exactly p, [SD 1.1] losslessness),
+ *   otherwise draw a bonus token from p_{ell+1};
+ *   draws use the inverse CDF in vocabulary order:
+ *   token = min{v : cumsum(w)_v > u * sum(w)} with u = u(r, pos0[r]+pos, 2).
+ *
+ *   R >= 0; gamma_max in [0, SD_MAX_GAMMA]; V in [8, SD_MAX_VOCAB], V % 8 == 0;
+ *   ld >= V, ld % 8 == 0; dtype SD_DTYPE_F32 or SD_DTYPE_BF16; temperature > 0
+ *   pos0        [R] int64 or NULL (all 0)
+ *   tgt_logits, drf_logits   row-major logit rows (dtype), see above
+ *   tgt_row0, drf_row0       [R] int32 first row of each request
+ *   draft_tokens [R][gamma_max] int32
+ *   ell          [R] int32 verified lengths, clamped to [0, gamma_max]
+ *                (typically sd_schedule's output, never read on the host)
+ * Outputs:
+ *   n_accepted  [R] int32
+ *   out_tokens  [R][gamma_max+1] int32: the n_accepted drafts, then the
+ *               replacement or bonus token, then -1 padding
+ *   status      [R] int32 SD_ST_* bits (written, not OR-ed)
+ *   probe_probs [R][gamma_max][2] fp32 (p_j(x_j), q_j(x_j)) for j <= ell, or NULL
+ *   row_stats   [R][2*gamma_max+1][2] fp32 (m, Z) with m = max(row)/T and
+ *               Z = sum exp(row/T - m): slots 0..gamma_max are target rows of
+ *               positions 1..gamma_max+1, slots gamma_max+1.. are draft rows of
+ *               positions 1..gamma_max; only slots inside the batch are written
+ * prof_start, prof_stop  optional HIP events (both or neither): recorded on
+ *             `stream` right before and after the row-statistics pass (the
+ *             bandwidth-bound kernel that streams every row once), so a caller
+ *             can time that pass alone.
+ * Degenerate data (mirrors the CPU reference): a token outside [0, V) at a
+ * tested position sets BAD_TOKEN and counts as a rejection; a needed row with
+ * NaN / +inf (NONFINITE) or all -inf (ZERO_Z) fails the request: n_accepted 0
+ * and every output token -1; an empty residual sets ZERO_RESIDUAL and the
+ * token is drawn from p_j*; q(x) = 0 sets ZERO_Q (accepted iff p(x) > 0).
+ */
+size_t sd_verify_workspace_size(int R, int gamma_max, int V);
+int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype,
+              float temperature, uint64_t seed, const int64_t* pos0,
+              const void* tgt_logits, const int32_t* tgt_row0,
+              const void* drf_logits, const int32_t* drf_row0,
+              const int32_t* draft_tokens, const int32_t* ell,
+              int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+              float* probe_probs, float* row_stats,
+              void* workspace, size_t workspace_bytes,
+              hipEvent_t prof_start, hipEvent_t prof_stop);
+
+/*
+ * sd_markov_draft - semi-autoregressive Markov head plus confidence head
+ * [DS innovation one, 2.1; SD move one].
+ *
+ * For k = 1..gamma, sequentially:
+ *   L_k[r]  = bf16_rne( U[r][k-1] + A_k[x_{k-1}] . C_k )     (bias in fp32)
+ *   x_k[r]  = inverse-CDF sample of softmax(L_k[r] / T) with u(r, pos0[r]+k, 0)
+ *   conf[r][k-1] = sigmoid( w[0:H] . h[r][k-1] + w[H:] . E[x_{k-1}] )
+ * starting from the target's anchor x_0 = x0[r] (Figure 1).  B_k(x) =
+ * A_k[x] . C_k is the V x V transition table stored low-rank.  L_k is written
+ * to q_logits and is exactly the draft distribution that was sampled, so
+ * q_logits can be handed to sd_verify as the draft rows (row (r*gamma + k-1),
+ * ld = V).
+ *
+ *   R >= 0; gamma in [0, SD_MAX_GAMMA]; V % 8 == 0, V in [8, SD_MAX_VOCAB];
+ *   rank % 32 == 0, 32 <= rank <= 256; H % 8 == 0; rank_e % 8 == 0;
+ *   temperature > 0
+ *   U        [R][gamma][V] bf16   parallel-backbone logits
+ *   A        [gamma][V][rank] bf16   A_k: row x is the left factor of B_k(x)
+ *   Ct       [gamma][V][rank] bf16   C_k transposed: row n is column n of C_k
+ *   x0       [R] int32 anchors
+ *   h        [R][gamma][H] bf16 backbone hidden states
+ *   E        [V][rank_e] bf16 Markov embedding;  w [H + rank_e] fp32
+ * Outputs: tokens [R][gamma] int32, q_logits [R][gamma][V] bf16,
+ *   conf [R][gamma] fp32, status [R] int32.
+ * Degenerate data: an anchor outside [0, V) sets BAD_TOKEN and contributes
+ * neither bias nor embedding; a row of L_k with NaN / +inf (NONFINITE) or all
+ * -inf (ZERO_Z) yields token -1 at that position (and BAD_TOKEN next).
+ */
+size_t sd_markov_draft_workspace_size(int R, int gamma, int V, int rank);
+int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
+                    float temperature, uint64_t seed, const int64_t* pos0,
+                    const uint16_t* U, const uint16_t* A, const uint16_t* Ct,
+                    const int32_t* x0, const uint16_t* h, int H,
+                    const uint16_t* E, int rank_e, const float* w,
+                    int32_t* tokens, uint16_t* q_logits, float* conf, int32_t* status,
+                    void* workspace, size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV_H */

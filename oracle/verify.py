@@ -79,7 +79,7 @@ def inverse_cdf(w, u):
     return tok, dist
 
 
-def verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=None):
+def verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=None, req_ids=None):
     """Run verification for every request.
 
     tgt / drf: 2-D arrays of logit rows (values exactly as the kernel sees
@@ -91,11 +91,13 @@ def verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=Non
     status[R] (bit-or per request), probe[R][gmax][2] = (p_j(x_j), q_j(x_j)),
     tgt_stats[R][gmax+1][2] and drf_stats[R][gmax][2] = (m, Z), alpha[R][gmax],
     and decisions: a list of (kind, r, j, distance) for every accept test and
-    every sample drawn.
+    every sample drawn.  req_ids[i] is the request index that keys request
+    i's uniforms (default i), so a subset of a larger batch can be checked.
     """
     R = len(ell)
     gmax = np.asarray(draft_tokens).shape[1]
     pos0 = np.zeros(R, np.int64) if pos0 is None else np.asarray(pos0, np.int64)
+    rid = np.arange(R) if req_ids is None else np.asarray(req_ids, np.int64)
     n_acc = np.zeros(R, np.int32)
     tokens = np.full((R, gmax + 1), -1, np.int32)
     status = np.zeros(R, np.int32)
@@ -138,7 +140,7 @@ def verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=Non
                 rejected_at = j
                 break
             p, q = p_rows[j - 1][x], q_rows[j - 1][x]
-            u = uniform(seed, r, int(pos0[r]) + j, DRAW_ACCEPT)
+            u = uniform(seed, int(rid[r]), int(pos0[r]) + j, DRAW_ACCEPT)
             if q == 0.0:
                 st |= ST_ZERO_Q
                 accept = p > 0.0
@@ -163,7 +165,7 @@ def verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=Non
             n = L
             w = p_rows[L]
             pos = L + 1
-        u2 = uniform(seed, r, int(pos0[r]) + pos, DRAW_CORRECT)
+        u2 = uniform(seed, int(rid[r]), int(pos0[r]) + pos, DRAW_CORRECT)
         tok, dist = inverse_cdf(w, u2)
         decisions.append(("sample", r, pos, dist))
         n_acc[r] = n

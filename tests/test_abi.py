@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every function include/sdv.h declares, and
+rejects bad arguments on the host before touching the GPU (no compute here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verification_amd as sdv
+from draft_verification_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sdv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"sd_schedule", "sd_verify", "sd_markov_draft"} <= set(names)
+    L = ctypes.CDLL(_lib._LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sdv.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert sdv.sd_abi_version() == 1
+    assert sdv.sd_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, 1, 2, 4, 8, 16):
+        assert sdv.sd_status_string(code) != "unknown status"
+    assert sdv.sd_status_string(12345) == "unknown status"
+
+
+def test_workspace_sizes():
+    ws = sdv.sd_verify_workspace_size(256, 11, 151936)
+    assert 0 < ws < 64 << 20
+    assert sdv.sd_verify_workspace_size(-1, 1, 8) == 0
+    assert sdv.sd_markov_draft_workspace_size(128, 16, 129280, 256) > 0
+
+
+N = None
+
+
+def _sched(R, g, mode, sps_len, conf=1, sps=1, ell=1, cap=None):
+    L = sdv.lib()
+    p = lambda x: ctypes.c_void_p(16) if x else None
+    return L.sd_schedule(None, R, g, None, p(conf), p(sps), sps_len, mode, p(cap), p(ell), N, N, N, N)
+
+
+def test_schedule_host_validation():
+    assert _sched(-1, 4, 0, 100) == _lib.SD_EINVAL
+    assert _sched(4, 256, 0, 10000) == _lib.SD_EUNSUPPORTED
+    assert _sched(2048, 16, 0, 40000) == _lib.SD_EUNSUPPORTED      # 32768 slots
+    assert _sched(4, 4, 3, 100) == _lib.SD_EINVAL                  # bad mode
+    assert _sched(4, 4, 2, 100) == _lib.SD_EINVAL                  # capped without cap_k
+    assert _sched(4, 4, 0, 19) == _lib.SD_ERANGE                   # table < R(1+g)
+    assert _sched(4, 4, 0, 20, ell=0) == _lib.SD_EINVAL
+
+
+def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=()):
+    L = sdv.lib()
+    P = lambda name: None if name in nulls else ctypes.c_void_p(256)
+    return L.sd_verify(None, R, g, V, ld, dt, T, 1, None, P("tgt"), P("t0"), P("drf"), P("d0"),
+                       P("toks"), P("ell"), P("nacc"), P("out"), P("st"), None, None,
+                       ctypes.c_void_p(ws_ptr), ws, None, None)
+
+
+def test_verify_host_validation():
+    assert _ver(V=60, ld=64) == _lib.SD_EINVAL
+    assert _ver(ld=32) == _lib.SD_EINVAL
+    assert _ver(ld=68) == _lib.SD_EINVAL
+    assert _ver(dt=5) == _lib.SD_EINVAL
+    assert _ver(T=0.0) == _lib.SD_EINVAL
+    assert _ver(T=float("nan")) == _lib.SD_EINVAL
+    assert _ver(g=300) == _lib.SD_EUNSUPPORTED
+    assert _ver(ws=16) == _lib.SD_ERANGE
+    assert _ver(ws_ptr=8) == _lib.SD_EINVAL                          # misaligned workspace
+    assert _ver(nulls=("tgt",)) == _lib.SD_EINVAL
+    assert _ver(nulls=("ell",)) == _lib.SD_EINVAL
+    assert _ver(R=0) == _lib.SD_OK                                  # nothing to do
+
+
+def _mk(R=2, g=2, V=64, rank=32, H=8, re_=8, T=1.0, ws=1 << 20, nulls=()):
+    L = sdv.lib()
+    P = lambda name: None if name in nulls else ctypes.c_void_p(256)
+    return L.sd_markov_draft(None, R, g, V, rank, T, 1, None, P("U"), P("A"), P("C"), P("x0"),
+                             P("h"), H, P("E"), re_, P("w"), P("tok"), P("ql"), P("conf"),
+                             P("st"), ctypes.c_void_p(256), ws)
+
+
+def test_markov_host_validation():
+    assert _mk(rank=48) == _lib.SD_EINVAL
+    assert _mk(rank=512) == _lib.SD_EUNSUPPORTED
+    assert _mk(V=100) == _lib.SD_EINVAL
+    assert _mk(H=12) == _lib.SD_EINVAL
+    assert _mk(T=-1.0) == _lib.SD_EINVAL
+    assert _mk(ws=8) == _lib.SD_ERANGE
+    assert _mk(nulls=("C",)) == _lib.SD_EINVAL
+    assert _mk(R=0) == _lib.SD_OK

@@ -1,0 +1,112 @@
+"""GPU parity of sd_schedule against the oracle: survival, l_r, B, n*, Theta
+must all be bit-identical."""
+
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_amd as sdv
+from oracle import schedule as OS
+from workloads import verify_config, sps_table
+
+pytestmark = pytest.mark.gpu
+
+MODES = [OS.EARLY_STOP, OS.GLOBAL_ARGMAX]
+
+
+def _run(conf, sps, mode, gamma_r=None, cap=None):
+    dev = "cuda"
+    c = torch.as_tensor(conf, dtype=torch.float32).to(dev).contiguous()
+    s = torch.as_tensor(sps, dtype=torch.float32).to(dev)
+    g = None if gamma_r is None else torch.as_tensor(gamma_r, dtype=torch.int32).to(dev)
+    k = None if cap is None else torch.tensor([int(cap)], dtype=torch.int32, device=dev)
+    out = sdv.sd_schedule(c, s, mode, gamma_r=g, cap_k=k)
+    torch.cuda.synchronize()
+    return {k2: (v.cpu().numpy() if v is not None else None) for k2, v in out.items()}
+
+
+def _check(conf, sps, mode, gamma_r=None, cap=None):
+    conf = np.asarray(conf, np.float32)
+    got = _run(conf, sps, mode, gamma_r, cap)
+    ref = OS.schedule(conf, sps, mode, gamma_r, cap_k=cap)
+    assert np.array_equal(got["ell"], ref["ell"]), (got["ell"], ref["ell"])
+    assert int(got["batch"][0]) == ref["B"]
+    assert int(got["n_sel"][0]) == ref["n_sel"]
+    assert float(got["theta"][0]) == ref["theta"]
+    assert np.array_equal(got["surv"], ref["surv"])
+    return ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "headline"])
+@pytest.mark.parametrize("mode", MODES)
+def test_schedule_workloads(name, mode):
+    inp = verify_config(name, device="cpu", V=64)  # only conf and sps are used
+    _check(inp["conf"].numpy(), inp["sps"].numpy(), mode)
+
+
+@pytest.mark.parametrize("levels", [None, (0.25, 0.5, 0.75, 1.0)])
+def test_schedule_random_cases(levels):
+    g = np.random.default_rng(11 if levels is None else 12)
+    for case in range(60):
+        R = int(g.integers(1, 48))
+        gmax = int(g.integers(1, 17))
+        if levels is None:
+            conf = (1 / (1 + np.exp(-g.normal(1.0, 1.5, (R, gmax))))).astype(np.float32)
+        else:
+            conf = g.choice(np.array(levels, np.float32), (R, gmax))
+        gam = g.integers(0, gmax + 1, R).astype(np.int32)
+        Bs = np.arange(1, R * (gmax + 1) + 1)
+        sps = (Bs / (1 + Bs / g.uniform(4, 64)) * (1 + 0.1 * (((Bs - 1) % 8) / 4.0 - 1))).astype(np.float32)
+        for mode in MODES:
+            _check(conf, sps, mode, gam)
+        _check(conf, sps, OS.CAPPED_TOPK, gam, cap=int(g.integers(0, R * gmax + 3)))
+
+
+def test_schedule_async_chain_on_device():
+    """Ragged async step: K from the previous confidences (global argmax), then
+    exactly K candidates by the current ones, chained through device memory."""
+    inp = verify_config("ragged", device="cpu", V=64)
+    conf, prev, sps, gam = inp["conf"], inp["conf_prev"], inp["sps"], inp["gamma_r"]
+    dev = "cuda"
+    first = sdv.sd_schedule(prev.to(dev), sps.to(dev), OS.GLOBAL_ARGMAX, gamma_r=gam.to(dev))
+    second = sdv.sd_schedule(conf.to(dev), sps.to(dev), OS.CAPPED_TOPK, gamma_r=gam.to(dev),
+                             cap_k=first["n_sel"])
+    torch.cuda.synchronize()
+    ref = OS.async_schedule(conf.numpy(), prev.numpy(), sps.numpy(), gam.numpy())
+    assert int(first["n_sel"].item()) == ref["cap_k"]
+    assert np.array_equal(second["ell"].cpu().numpy(), ref["ell"])
+    assert int(second["batch"].item()) == ref["B"]
+    assert float(second["theta"].item()) == ref["theta"]
+
+
+def test_schedule_maximum_slots_and_subnormal_survival():
+    g = np.random.default_rng(13)
+    R, gmax = 1024, 16                          # R * gmax = 16384, the limit
+    conf = (1 / (1 + np.exp(-g.normal(0.0, 3.0, (R, gmax))))).astype(np.float32)
+    conf[:8] = np.float32(0.004)                # survivals reach the fp32 subnormal range
+    sps = sps_table(R * (gmax + 1), 256, 0.08, 64).numpy()
+    for mode in MODES:
+        _check(conf, sps, mode)
+    _check(conf, sps, OS.CAPPED_TOPK, cap=R * gmax - 3)
+
+
+def test_schedule_degenerate_sizes():
+    sps = np.ones(64, np.float32)
+    got = _run(np.zeros((5, 0), np.float32), sps, OS.EARLY_STOP)
+    assert np.all(got["ell"] == 0) and int(got["batch"][0]) == 5 and float(got["theta"][0]) == 0.0
+    conf = np.zeros((3, 4), np.float32)           # zero confidence: Theta stays 0
+    _check(conf, sps, OS.EARLY_STOP)
+    _check(conf, sps, OS.GLOBAL_ARGMAX)
+    _check(np.ones((3, 4), np.float32), sps, OS.EARLY_STOP)
+
+
+def test_schedule_host_errors():
+    dev = "cuda"
+    c = torch.rand((4, 4), device=dev)
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_schedule(c, torch.ones(10, device=dev), OS.EARLY_STOP)   # table < 20
+    assert e.value.code == -2
+    with pytest.raises(sdv.SdvError):
+        sdv.sd_schedule(c, torch.ones(20, device=dev), 7)
+    with pytest.raises(sdv.SdvError):
+        sdv.sd_schedule(c, torch.ones(20, device=dev), OS.CAPPED_TOPK)  # no cap_k

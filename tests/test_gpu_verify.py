@@ -1,0 +1,166 @@
+"""GPU parity of sd_verify against the oracle.
+
+Accepted lengths, emitted tokens and status bits must match exactly, except
+for requests with a decision the oracle marks near-boundary (distance < 1e-6);
+(m, Z) per row and (p(x), q(x)) per tested position within 1e-5 relative.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_amd as sdv
+from oracle import schedule as OS
+from workloads import verify_config, verify_inputs
+from tests.parity_util import (oracle_verify_subset, compare_verify, check_stats, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_verify(inp, ell_dev, probe=True, stats=True, **kw):
+    out = sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
+                        inp["draft_tokens"], ell_dev, inp["V"], inp["temperature"], inp["seed"],
+                        pos0=inp.get("pos0"), probe=probe, stats=stats, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _to_cuda(inp):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def _full_check(inp, ell_dev, reqs=None):
+    gpu = _gpu_verify(inp, ell_dev)
+    ell = to_np(ell_dev)
+    R = inp["R"]
+    reqs = list(range(R)) if reqs is None else list(reqs)
+    ora = oracle_verify_subset(inp, reqs, ell)
+    n_dec, n_near, mism = compare_verify(gpu, ora, reqs)
+    check_stats(gpu, ora, reqs, ell, inp["gmax"])
+    print(f"decisions={n_dec} near-boundary={n_near} diverged={mism}")
+    assert mism <= max(1, 1e-4 * n_dec)
+    return gpu, ora
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+@pytest.mark.parametrize("mode", ["full", "early", "argmax"])
+def test_verify_workloads(name, mode):
+    inp = _to_cuda(verify_config(name, device="cpu"))
+    R, g = inp["R"], inp["gmax"]
+    if mode == "full":
+        ell = torch.full((R,), g, dtype=torch.int32, device="cuda")
+    else:
+        m = OS.EARLY_STOP if mode == "early" else OS.GLOBAL_ARGMAX
+        ell = sdv.sd_schedule(inp["conf"], inp["sps"], m)["ell"]
+    _full_check(inp, ell)
+
+
+def test_verify_ragged_vocab_and_padded_rows():
+    # V not a multiple of the 16384-element chunk nor of 64, ld > V, fp32 and bf16
+    for dtype in (torch.float32, torch.bfloat16):
+        inp = _to_cuda(verify_inputs(R=7, gmax=5, V=40008, ld=40016, dtype=dtype, sigma_t=2.0,
+                                     zipf=True, sigma_d=(0.3, 2.0), seed=77))
+        ell = torch.tensor([0, 1, 2, 3, 4, 5, 5], dtype=torch.int32, device="cuda")
+        _full_check(inp, ell)
+
+
+def test_verify_temperature_and_positions():
+    inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
+                                 zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
+    inp["pos0"] = torch.arange(9, dtype=torch.int64, device="cuda") * 1000 + 17
+    ell = torch.full((9,), 6, dtype=torch.int32, device="cuda")
+    _full_check(inp, ell)
+
+
+def test_verify_packed_layout():
+    # rows of consecutive requests packed back to back (no reserved slots)
+    inp = _to_cuda(verify_inputs(R=6, gmax=4, V=4096, dtype=torch.bfloat16, sigma_t=2.0,
+                                 seed=79))
+    ell_h = np.array([4, 0, 2, 3, 1, 4])
+    t0 = np.concatenate([[0], np.cumsum(ell_h + 1)[:-1]])
+    d0 = np.concatenate([[0], np.cumsum(ell_h)[:-1]])
+    tgt = torch.cat([inp["tgt"][r * 5:r * 5 + ell_h[r] + 1] for r in range(6)])
+    drf = torch.cat([inp["drf"][r * 4:r * 4 + ell_h[r]] for r in range(6)])
+    inp.update(tgt=tgt.contiguous(), drf=drf.contiguous(),
+               tgt_row0=torch.as_tensor(t0, dtype=torch.int32, device="cuda"),
+               drf_row0=torch.as_tensor(d0, dtype=torch.int32, device="cuda"))
+    _full_check(inp, torch.as_tensor(ell_h, dtype=torch.int32, device="cuda"))
+
+
+def test_verify_headline_full_block_sampled():
+    """R=256, gamma=11, V=151936 bf16 at the full block, as timed by bench.py;
+    the oracle checks a sample of requests, every request is checked for
+    structural validity."""
+    inp = verify_config("headline", device="cuda")
+    R, g = inp["R"], inp["gmax"]
+    sched = sdv.sd_schedule(inp["conf"], inp["sps"], OS.GLOBAL_ARGMAX)
+    ell = sched["ell"]
+    assert int(sched["batch"].item()) == R * (g + 1)   # the global argmax takes the full block
+    gpu, _ = _full_check(inp, ell, reqs=[0, 1, 57, 128, 200, 255])
+    n_acc = to_np(gpu["n_acc"])
+    toks = to_np(gpu["tokens"])
+    drafts = to_np(inp["draft_tokens"])
+    assert np.all(to_np(gpu["status"]) == 0)
+    for r in range(R):
+        n = n_acc[r]
+        assert 0 <= n <= g
+        assert np.array_equal(toks[r, :n], drafts[r, :n])
+        assert 0 <= toks[r, n] < inp["V"]
+        assert np.all(toks[r, n + 1:] == -1)
+
+
+def test_verify_ragged_async_sampled():
+    """R=512, gamma_r in 1..16, reserved slots past gamma_r hold NaN; schedule
+    with the async capacity chain, then verify."""
+    inp = verify_config("ragged", device="cuda")
+    first = sdv.sd_schedule(inp["conf_prev"], inp["sps"], OS.GLOBAL_ARGMAX, gamma_r=inp["gamma_r"])
+    sched = sdv.sd_schedule(inp["conf"], inp["sps"], OS.CAPPED_TOPK, gamma_r=inp["gamma_r"],
+                            cap_k=first["n_sel"])
+    ell = sched["ell"]
+    gpu, _ = _full_check(inp, ell, reqs=[0, 3, 99, 256, 400, 511])
+    assert np.all(to_np(gpu["status"]) == 0)   # no NaN slot was read
+
+
+def test_verify_degenerate_rows_and_tokens():
+    V, g = 2048, 3
+    inp = _to_cuda(verify_inputs(R=8, gmax=g, V=V, dtype=torch.float32, sigma_t=2.0, seed=80))
+    tgt, drf, toks = inp["tgt"], inp["drf"], inp["draft_tokens"]
+    tgt[0 * 4 + 1, 10] = float("nan")                # r0: NaN in a needed target row
+    tgt[1 * 4 + 3, :] = float("-inf")               # r1: bonus row all -inf
+    toks[2, 0] = V + 5                              # r2: bad token at position 1
+    drf[3 * 3 + 0, int(toks[3, 0])] = float("-inf")  # r3: q(x) = 0 at position 1
+    tgt[4 * 4 + 2, 0] = float("inf")                # r4: +inf in a needed row
+    tgt[5 * 4 + 3, 0] = float("nan")                # r5: NaN only past l_r -> unread
+    drf[6 * 3:6 * 3 + 3] = tgt[6 * 4:6 * 4 + 3]     # r6: p == q everywhere
+    ell = torch.tensor([3, 3, 3, 3, 3, 2, 3, 0], dtype=torch.int32, device="cuda")
+    gpu, ora = _full_check(inp, ell)
+    st = to_np(gpu["status"])
+    assert st[0] == sdv.SD_ST_NONFINITE and st[1] == sdv.SD_ST_ZERO_Z
+    assert st[2] & sdv.SD_ST_BAD_TOKEN and st[3] & sdv.SD_ST_ZERO_Q
+    assert st[4] == sdv.SD_ST_NONFINITE and st[5] == 0
+    assert to_np(gpu["n_acc"])[6] == 3
+
+
+def test_verify_repeatable():
+    inp = _to_cuda(verify_config("mid", device="cpu"))
+    ell = torch.full((inp["R"],), inp["gmax"], dtype=torch.int32, device="cuda")
+    a = _gpu_verify(inp, ell)
+    b = _gpu_verify(inp, ell)
+    for k in ("n_acc", "tokens", "status", "probe", "row_stats"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_verify_host_errors():
+    inp = _to_cuda(verify_inputs(R=2, gmax=2, V=64, dtype=torch.float32, seed=81))
+    ell = torch.full((2,), 2, dtype=torch.int32, device="cuda")
+    with pytest.raises(sdv.SdvError):
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
+                      inp["draft_tokens"], ell, 60, 1.0, 1)           # V % 8 != 0
+    with pytest.raises(sdv.SdvError):
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
+                      inp["draft_tokens"], ell, 64, 0.0, 1)           # temperature 0
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
+                      inp["draft_tokens"], ell, 64, 1.0, 1, workspace=small)
+    assert e.value.code == -2
