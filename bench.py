@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify step on one MI355X.
+
+Metric: verify rows/s at R=256, gamma=11, V=151936 bf16, and the fraction of
+the HBM roofline reached by the row-statistics pass (the kernel that streams
+every verify and draft row once).
+
+One step = sd_schedule (global argmax over the step's confidences; with this
+throughput table it keeps the full block, B = R * (1 + gamma) = 3072 rows)
+followed by sd_verify on the rows the schedule chose (ell read on the device,
+no host round trip).  Inputs are resident in HBM before timing starts; two
+input sets of 1.79 GB alternate between steps so the 256 MB last-level cache
+cannot serve repeats.
+
+Also reported: the oracle timed on the host's cores on a bounded sample of
+the same step (cpu_baseline), and the Markov drafting head at R=128,
+gamma=16, V=129280, rank 256 (markov_draft).
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_partials_headline.json")
+KERNEL_SOURCE = os.path.join(ROOT, "draft_verification_amd", "csrc", "verify.hip")
+
+
+class HipEvents:
+    """Raw HIP events on the runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(bytes_per_launch):
+    """HBM traffic of the row-statistics kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, ell, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    full schedule plus verification of as many requests as fit the budget."""
+    import numpy as np
+    from oracle import schedule as OS
+    from tests.parity_util import oracle_verify_subset, to_np
+
+    conf = to_np(inp["conf"])
+    sps = to_np(inp["sps"])
+    t0 = time.perf_counter()
+    OS.schedule(conf, sps, OS.GLOBAL_ARGMAX)
+    t_sched = time.perf_counter() - t0
+    R = inp["R"]
+    done, t_ver = 0, 0.0
+    order = np.random.default_rng(0).permutation(R)
+    while done < R and (t_ver < budget_s or done < 8):
+        reqs = [int(x) for x in order[done:done + 8]]
+        t0 = time.perf_counter()
+        oracle_verify_subset(inp, reqs, ell)
+        t_ver += time.perf_counter() - t0
+        done += len(reqs)
+    rows_sample = int(sum(1 + ell[r] for r in order[:done]))
+    step_s = t_sched + t_ver * (R / done)
+    B = int(sum(1 + e for e in ell))
+    threads = os.environ.get("OMP_NUM_THREADS", "unset")
+    return {
+        "value": B / step_s,
+        "unit": "rows/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"full schedule of all {R} requests ({t_sched:.2f} s) + verification of {done} of "
+                   f"{R} requests ({rows_sample} target rows, {t_ver:.1f} s), scaled to the whole "
+                   f"step; fp64 NumPy elementwise work runs on one thread (OMP_NUM_THREADS={threads}, "
+                   f"host reports {os.cpu_count()} CPUs)"),
+    }
+
+
+def bench_markov(sdv, torch, steps, hip):
+    from workloads import markov_config
+    inp = markov_config(device="cuda")
+    R, g, V, rank = inp["R"], inp["gamma"], inp["V"], inp["rank"]
+    dev = "cuda"
+    out = dict(tokens=torch.empty((R, g), dtype=torch.int32, device=dev),
+               q_logits=torch.empty((R, g, V), dtype=torch.bfloat16, device=dev),
+               conf=torch.empty((R, g), dtype=torch.float32, device=dev),
+               status=torch.empty(R, dtype=torch.int32, device=dev))
+    ws = torch.empty(max(sdv.sd_markov_draft_workspace_size(R, g, V, rank), 256), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: sdv.sd_markov_draft(inp["U"], inp["A"], inp["Ct"], inp["x0"], inp["h"], inp["E"],
+                                       inp["w"], 1.0, inp["seed"], workspace=ws, out=out)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    n = max(3, min(steps, 20))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    hbm = (2 * g * V * rank + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # Ct + U + L + h
+    flops = 2.0 * R * rank * V * g
+    return {"workload": f"R={R}, gamma={g}, V={V}, rank={rank}, H=4096, bf16",
+            "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
+            "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
+            "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
+            "launches": 2 * g + 1}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-markov", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no "
+              "multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import draft_verification_amd as sdv
+    from workloads import verify_config
+    from workloads.synth import headline_bytes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+    print("generating inputs", file=sys.stderr, flush=True)
+    sets = [verify_config("headline", device=dev), verify_config("headline", device=dev, data_shift=1)]
+    R, g, V = sets[0]["R"], sets[0]["gmax"], sets[0]["V"]
+    torch.cuda.synchronize()
+
+    # preallocated outputs and workspaces: nothing is allocated while timing
+    def outs():
+        return (dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+                     batch=torch.empty(1, dtype=torch.int32, device=dev),
+                     n_sel=torch.empty(1, dtype=torch.int32, device=dev),
+                     theta=torch.empty(1, dtype=torch.float64, device=dev),
+                     surv=torch.empty((R, g), dtype=torch.float32, device=dev)),
+                dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                     tokens=torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+                     status=torch.empty(R, dtype=torch.int32, device=dev)))
+    bufs = [outs() for _ in sets]
+    ws = torch.empty(sdv.sd_verify_workspace_size(R, g, V), dtype=torch.uint8, device=dev)
+
+    def step(i, prof=None):
+        inp = sets[i % len(sets)]
+        so, vo = bufs[i % len(sets)]
+        sch = sdv.sd_schedule(inp["conf"], inp["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so)
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                      sch["ell"], V, inp["temperature"], inp["seed"], workspace=ws, out=vo,
+                      prof_events=prof)
+
+    hip = HipEvents()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    batch = [int(b[0]["batch"].item()) for b in bufs]
+    assert all(b == R * (g + 1) for b in batch), batch
+
+    K = args.steps
+    kev = hip.create(2 * K)
+    print(f"timing {K} steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        step(i, prof=(kev[2 * i], kev[2 * i + 1]))
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    k_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(K)]
+    hip.destroy(kev)
+    ms_per_step = ms_total / K
+    rows = R * (g + 1)
+    value = rows * K / (ms_total / 1e3)
+
+    # schedule alone (the rest of the step is verification)
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    so = bufs[0][0]
+    s0.record()
+    for _ in range(K):
+        sdv.sd_schedule(sets[0]["conf"], sets[0]["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so)
+    s1.record()
+    torch.cuda.synchronize()
+    sched_us = s0.elapsed_time(s1) / K * 1e3
+
+    bytes_launch = headline_bytes(R, g, V)
+    k_avg = float(np.mean(k_ms))
+    achieved = bytes_launch / (k_avg / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(bytes_launch),
+                "kernel": "k_row_partials<bf16>", "kernel_avg_us": round(k_avg * 1e3, 2),
+                "bytes_per_launch": bytes_launch}
+
+    result = {
+        "metric": "verify rows/s at R=256,γ=11,V=151936 bf16; % of HBM roofline",
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "headline schedule+verify step: R=256 requests, gamma=11 drafts, "
+                               "V=151936, bf16 logits, full block B=3072 target + 2816 draft rows",
+                   "R": R, "gamma": g, "V": V, "verify_rows": rows, "draft_rows": R * g,
+                   "input_sets": len(sets)},
+        "roofline": roofline,
+        "breakdown_us": {"step": round(ms_per_step * 1e3, 1), "schedule": round(sched_us, 1),
+                         "row_stats_kernel": round(k_avg * 1e3, 1)},
+    }
+    if not args.no_markov:
+        print("markov head", file=sys.stderr, flush=True)
+        result["markov_draft"] = bench_markov(sdv, torch, K, hip)
+    if not args.no_cpu_baseline:
+        print("cpu baseline (oracle)", file=sys.stderr, flush=True)
+        ell = bufs[0][0]["ell"].cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(sets[0], ell)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

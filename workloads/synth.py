@@ -152,13 +152,14 @@ def verify_inputs(R, gmax, V, dtype=torch.bfloat16, sigma_t=2.0, zipf=False,
     )
 
 
-def verify_config(name, device="cpu", **over):
-    """One of the named schedule + verify workloads."""
+def verify_config(name, device="cpu", data_shift=0, **over):
+    """One of the named schedule + verify workloads; data_shift != 0 draws an
+    independent input set of the same workload."""
     cfg = dict(CONFIGS[name])
     ragged = cfg.pop("ragged", False)
     seed_off = cfg.pop("seed_off")
     cfg.update(over)
-    seed = BASE_SEED + seed_off
+    seed = BASE_SEED + seed_off + 1000003 * data_shift
     if ragged and "gamma_r" not in over:
         g = _gen("cpu", seed + 1000)
         cfg["gamma_r"] = torch.randint(1, cfg["gmax"] + 1, (cfg["R"],), generator=g, dtype=torch.int32)
