@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     sd_abi_version,
     sd_status_string,
     sd_schedule,
+    sd_schedule_workspace_size,
     sd_verify,
     sd_verify_workspace_size,
     sd_markov_draft,

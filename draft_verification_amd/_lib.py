@@ -34,7 +34,8 @@ SD_ST_ZERO_RESIDUAL = 8
 SD_ST_ZERO_Q = 16
 
 EXPORTS = (
-    "sd_abi_version", "sd_status_string", "sd_schedule", "sd_verify_workspace_size",
+    "sd_abi_version", "sd_status_string", "sd_schedule_workspace_size", "sd_schedule",
+    "sd_verify_workspace_size",
     "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
 )
 
@@ -64,7 +65,9 @@ def lib():
     L.sd_status_string.restype = ctypes.c_char_p
     L.sd_status_string.argtypes = [_I]
     L.sd_schedule.restype = _I
-    L.sd_schedule.argtypes = [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
+    L.sd_schedule_workspace_size.restype = _SZ
+    L.sd_schedule_workspace_size.argtypes = [_I, _I]
+    L.sd_schedule.argtypes = [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ]
     L.sd_verify_workspace_size.restype = _SZ
     L.sd_verify_workspace_size.argtypes = [_I, _I, _I]
     L.sd_verify.restype = _I
@@ -119,7 +122,12 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, stream=None):
+def sd_schedule_workspace_size(R, gmax):
+    return lib().sd_schedule_workspace_size(R, gmax)
+
+
+def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, workspace=None,
+                stream=None):
     """Run the scheduler.  conf [R][gmax] fp32, sps fp32, gamma_r [R] int32 or
     None, cap_k a 1-element int32 device tensor (CAPPED_TOPK).  Returns a dict
     of device tensors: ell, batch, n_sel, theta, surv."""
@@ -131,11 +139,13 @@ def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, 
     n_sel = o.get("n_sel", torch.empty(1, dtype=torch.int32, device=dev))
     theta = o.get("theta", torch.empty(1, dtype=torch.float64, device=dev))
     sv = o.get("surv", torch.empty((R, gmax), dtype=torch.float32, device=dev)) if surv else None
+    ws = workspace if workspace is not None else _workspace(sd_schedule_workspace_size(R, gmax), dev)
     code = lib().sd_schedule(
         _stream(stream), R, gmax, _ptr(gamma_r, torch.int32, "gamma_r"),
         _ptr(conf, torch.float32, "conf"), _ptr(sps, torch.float32, "sps"), sps.numel(), int(mode),
         _ptr(cap_k, torch.int32, "cap_k"), _ptr(ell, torch.int32), _ptr(batch, torch.int32),
-        _ptr(n_sel, torch.int32), _ptr(theta, torch.float64), _ptr(sv, torch.float32))
+        _ptr(n_sel, torch.int32), _ptr(theta, torch.float64), _ptr(sv, torch.float32),
+        ws.data_ptr(), ws.numel())
     _check("sd_schedule", code)
     return dict(ell=ell, batch=batch, n_sel=n_sel, theta=theta, surv=sv)
 

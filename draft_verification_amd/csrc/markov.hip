@@ -70,7 +70,10 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
   // LDS: gathered A rows during the GEMM, then the fp32 output tile.
   constexpr int kAbytes = kTileM * (kMaxRank + kApad) * 2;
   constexpr int kGbytes = kTileM * (kTileN + kGpad) * 4;
+  constexpr int kEpiPasses = kTileM / 16;
+  constexpr int kGatherPerThread = kTileM * (kMaxRank / 8) / kThreads;
   __shared__ __align__(16) unsigned char lds[kAbytes > kGbytes ? kAbytes : kGbytes];
+  __shared__ int s_xp[kTileM];
   uint16_t* sA = (uint16_t*)lds;
   float* sG = (float*)lds;
 
@@ -84,8 +87,16 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
   const uint16_t* Ak = A + (size_t)(k - 1) * vr;
   const uint16_t* Ck = Ct + (size_t)(k - 1) * vr;
 
-  // B fragments straight from HBM: lane l holds column (l % 16) of its
-  // 16-column block, K values [32*ks + 8*(l/16), +8).
+  // Every HBM read of the workgroup is issued up front so that their
+  // latencies overlap: previous tokens, B fragments, the U tile, the A rows.
+  if (tid < kTileM) {
+    const int r = m0 + tid;
+    int xp = -1;
+    if (r < R) xp = (k == 1) ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
+    s_xp[tid] = (xp >= 0 && xp < V) ? xp : -1;  // out of range: no Markov bias
+  }
+  // B fragments: lane l holds column (l % 16) of its 16-column block,
+  // K values [32*ks + 8*(l/16), +8).
   uint4 bfrag[2][kMaxRank / 32];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -93,24 +104,37 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
 #pragma unroll
     for (int ks = 0; ks < kMaxRank / 32; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (ks < ksteps && col < V)
-        v = sdv::ld_nt(Ck + (size_t)col * rank + ks * 32 + (lane >> 4) * 8);
+      if (ks < ksteps && col < V) v = sdv::ld_nt(Ck + (size_t)col * rank + ks * 32 + (lane >> 4) * 8);
       bfrag[nb][ks] = v;
     }
   }
-
-  // Gather the previous tokens' A rows into LDS (zeros for rows past R and
-  // for out-of-range previous tokens: no Markov bias).
+  // U for the epilogue: 16 threads per row, 8 columns each, 16 rows per pass
+  const int seg = tid & 15;
+  const int ecol = n0 + seg * 8;
+  uint4 upre[kEpiPasses];
+#pragma unroll
+  for (int pass = 0; pass < kEpiPasses; ++pass) {
+    const int r = m0 + pass * 16 + (tid >> 4);
+    upre[pass] = (r < R && ecol < V) ? sdv::ld_nt(U + ((size_t)r * gamma + (k - 1)) * V + ecol)
+                                     : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();  // s_xp
   const int vec_per_row = rank / 8;
-  for (int idx = tid; idx < kTileM * vec_per_row; idx += kThreads) {
-    const int mr = idx / vec_per_row, v = idx % vec_per_row;
-    const int r = m0 + mr;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < R) {
-      const int xp = (k == 1) ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
-      if (xp >= 0 && xp < V) val = *(const uint4*)(Ak + (size_t)xp * rank + v * 8);
+  const int total = kTileM * vec_per_row;
+  uint4 gat[kGatherPerThread];
+#pragma unroll
+  for (int i = 0; i < kGatherPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    gat[i] = make_uint4(0, 0, 0, 0);
+    if (idx < total) {
+      const int xp = s_xp[idx / vec_per_row];
+      if (xp >= 0) gat[i] = *(const uint4*)(Ak + (size_t)xp * rank + (idx % vec_per_row) * 8);
     }
-    *(uint4*)(sA + mr * lda + v * 8) = val;
+  }
+#pragma unroll
+  for (int i = 0; i < kGatherPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < total) *(uint4*)(sA + (idx / vec_per_row) * lda + (idx % vec_per_row) * 8) = gat[i];
   }
   __syncthreads();
 
@@ -148,18 +172,17 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
         sG[(mb * 16 + (lane >> 4) * 4 + i) * ldg + wave * 32 + nb * 16 + (lane & 15)] = acc[mb][nb][i];
   __syncthreads();
 
-  // Epilogue: 16 threads per row, 8 columns each; 16 rows per pass.
-  const int seg = tid & 15;
-  const int col = n0 + seg * 8;
-  for (int pass = 0; pass < kTileM / 16; ++pass) {
+  // Epilogue: L = bf16(U + G), stored; per-(row, tile) partial (max, sum).
+#pragma unroll
+  for (int pass = 0; pass < kEpiPasses; ++pass) {
     const int mr = pass * 16 + (tid >> 4);
     const int r = m0 + mr;
     float m = kNegInf, s = 0.0f;
     float vals[8];
-    const bool live = (r < R) && (col < V);
+    const bool live = (r < R) && (ecol < V);
     if (live) {
-      const size_t off = ((size_t)r * gamma + (k - 1)) * V + col;
-      const uint4 u = sdv::ld_nt(U + off);
+      const size_t off = ((size_t)r * gamma + (k - 1)) * V + ecol;
+      const uint4 u = upre[pass];
       const float* g = sG + mr * ldg + seg * 8;
       const float uu[8] = {sdv::bf16lo(u.x), sdv::bf16hi(u.x), sdv::bf16lo(u.y), sdv::bf16hi(u.y),
                            sdv::bf16lo(u.z), sdv::bf16hi(u.z), sdv::bf16lo(u.w), sdv::bf16hi(u.w)};

@@ -7,16 +7,26 @@
 // history page, DSpark "move two": a_{r,j} is the product of the per-position
 // confidences up to j.
 //
-// One workgroup of 1024 threads does everything in LDS (the problem is at most
-// 16384 candidates, and latency-bound): keys are uint64 so that one ascending
-// integer sort orders by survival descending, then request, then position.
+// Keys are uint64 so that one ascending integer order sorts by survival
+// descending, then request, then position; they are unique.  Two kernels:
+//   k_sched_rank    many workgroups: each rebuilds every key in LDS (one
+//                   thread per request, fp32 products left to right) and
+//                   ranks 16 candidates by counting the smaller keys, 16
+//                   threads per candidate; writes sorted[rank] = key.  Sorting
+//                   by counting is N^2 work, but spread over the whole chip it
+//                   beats any single-CU network for these sizes (N <= 16384).
+//   k_sched_select  one workgroup: the sorted keys in registers, the
+//                   fixed-point tau scan, Theta, the mode's n*, and l_r.
 #include "sdv_common.h"
 #include "sdv_host.h"
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;  // k_sched_select
 constexpr int kWaves = kThreads / 64;
+constexpr int kRankThreads = 256;
+constexpr int kRankCand = 16;   // candidates per ranking workgroup
+constexpr int kRankSegs = kRankThreads / kRankCand;
 
 // key = (~bits(a)) << 32 | r << 8 | j.  a >= 0, so its bit pattern grows with
 // a and the complement sorts larger survival first.
@@ -35,18 +45,68 @@ __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, int lane) {
   uint64_t incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    uint64_t t = __shfl_up(incl, o, 64);
+    const uint64_t t = __shfl_up(incl, o, 64);
     if (lane >= o) incl += t;
   }
   return incl - v;
 }
 
-__global__ __launch_bounds__(kThreads) void k_schedule(
+
+// Survival products of request r into keys[r*gmax .. r*gmax + gmax): fp32,
+// left to right; slots past gamma_r get the largest key.
+__device__ __forceinline__ int request_keys(int r, int gmax, const int32_t* gamma_r,
+                                            const float* conf, uint64_t* keys, float* surv) {
+  const int g = gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
+  float a = 1.0f;
+  for (int j = 1; j <= gmax; ++j) {
+    const int i = r * gmax + (j - 1);
+    uint64_t key = ~0ull;
+    float out = 0.0f;
+    if (j <= g) {
+      a = a * conf[i];
+      key = make_key(a, r, j);
+      out = a;
+    }
+    keys[i] = key;
+    if (surv) surv[i] = out;
+  }
+  return g;
+}
+
+__global__ __launch_bounds__(kRankThreads) void k_sched_rank(
     int R, int gmax, const int32_t* __restrict__ gamma_r, const float* __restrict__ conf,
-    const float* __restrict__ sps, int mode, const int32_t* __restrict__ cap_k,
+    float* __restrict__ surv, uint64_t* __restrict__ sorted) {
+  extern __shared__ uint64_t keys[];
+  __shared__ int part[kRankSegs][kRankCand];
+  const int tid = threadIdx.x;
+  const int nslots = R * gmax;
+  float* my_surv = blockIdx.x == 0 ? surv : nullptr;  // one workgroup writes it
+  for (int r = tid; r < R; r += kRankThreads) request_keys(r, gmax, gamma_r, conf, keys, my_surv);
+  __syncthreads();
+  const int cl = tid % kRankCand, seg = tid / kRankCand;
+  const int cand = blockIdx.x * kRankCand + cl;
+  const uint64_t mine = cand < nslots ? keys[cand] : ~0ull;
+  const int len = (nslots + kRankSegs - 1) / kRankSegs;
+  const int i0 = seg * len, i1 = min(nslots, i0 + len);
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += keys[i] < mine ? 1 : 0;
+  part[seg][cl] = cnt;
+  __syncthreads();
+  if (tid < kRankCand && mine != ~0ull) {
+    int rank = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kRankSegs; ++s2) rank += part[s2][tid];
+    sorted[rank] = mine;
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void k_sched_select(
+    int R, int gmax, const int32_t* __restrict__ gamma_r, const float* __restrict__ sps,
+    int mode, const int32_t* __restrict__ cap_k, const uint64_t* __restrict__ sorted,
     int32_t* __restrict__ ell, int32_t* __restrict__ batch_out, int32_t* __restrict__ n_sel_out,
-    double* __restrict__ theta_out, float* __restrict__ surv, int npad) {
-  __shared__ uint64_t keys[SD_MAX_SCHED_SLOTS];
+    double* __restrict__ theta_out) {
+  __shared__ int ell_lds[SD_MAX_SCHED_SLOTS];
   __shared__ uint64_t wave_tot[kWaves];
   __shared__ int s_count, s_fail, s_nstar;
   __shared__ double s_best_theta[kWaves];
@@ -55,82 +115,54 @@ __global__ __launch_bounds__(kThreads) void k_schedule(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) { s_count = 0; s_fail = 0x7FFFFFFF; }
   __syncthreads();
-
-  // 1. survival products, left to right in fp32, one thread per request.
   int my_count = 0;
   for (int r = tid; r < R; r += kThreads) {
-    const int g = gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
-    float a = 1.0f;
-    for (int j = 1; j <= gmax; ++j) {
-      uint64_t key = ~0ull;
-      float out = 0.0f;
-      if (j <= g) {
-        a = a * conf[(size_t)r * gmax + (j - 1)];
-        key = make_key(a, r, j);
-        out = a;
-      }
-      keys[r * gmax + (j - 1)] = key;
-      if (surv) surv[(size_t)r * gmax + (j - 1)] = out;
-    }
-    my_count += g;
+    my_count += gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
+    ell_lds[r] = 0;
   }
-  for (int i = R * gmax + tid; i < npad; i += kThreads) keys[i] = ~0ull;
   if (my_count) atomicAdd(&s_count, my_count);
   __syncthreads();
   const int N = s_count;
+  const int i0 = tid * E;
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (i0 + e < N) ? sorted[i0 + e] : ~0ull;
 
-  // 2. bitonic sort of npad keys, ascending.
-  for (int k = 2; k <= npad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < (npad >> 1); t += kThreads) {
-        const int i = 2 * t - (t & (j - 1));
-        const int l = i + j;
-        const uint64_t x = keys[i], y = keys[l];
-        const bool asc = (i & k) == 0;
-        if ((x > y) == asc) { keys[i] = y; keys[l] = x; }
-      }
-      __syncthreads();
-    }
-  }
-
-  // 3. fixed-point tau scan over the sorted order: thread t owns the
-  //    contiguous positions [t*seg, (t+1)*seg).
-  const int seg = (npad + kThreads - 1) / kThreads;
-  const int i0 = tid * seg;
+  // 3. fixed-point tau scan over the sorted order.
   uint64_t my_sum = 0;
-  for (int s = 0; s < seg; ++s) {
-    const int i = i0 + s;
-    if (i < N) my_sum += key_fixed_point(keys[i]);
-  }
-  uint64_t excl = wave_excl_scan_u64(my_sum, lane);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (i0 + e < N) my_sum += key_fixed_point(key[e]);
+  const uint64_t excl = wave_excl_scan_u64(my_sum, lane);
   if (lane == 63) wave_tot[wave] = excl + my_sum;
   __syncthreads();
   if (wave == 0) {
-    uint64_t v = lane < kWaves ? wave_tot[lane] : 0;
-    uint64_t e = wave_excl_scan_u64(v, lane);
+    const uint64_t v = lane < kWaves ? wave_tot[lane] : 0;
+    const uint64_t e = wave_excl_scan_u64(v, lane);
     if (lane < kWaves) wave_tot[lane] = e;
   }
   __syncthreads();
-  uint64_t T = excl + wave_tot[wave];
+  const uint64_t T0 = excl + wave_tot[wave];
 
   // 4. Theta_n = (T_n * 2^-32) * SPS[R + n - 1]; first decline and argmax.
-  double best = 0.0;   // Theta_0 = 0 at n = 0
+  double best = 0.0;  // Theta_0 = 0 at n = 0
   int best_n = 0;
   int fail = 0x7FFFFFFF;
-  for (int s = 0; s < seg; ++s) {
-    const int i = i0 + s;
-    if (i >= N) break;
-    const uint64_t q = key_fixed_point(keys[i]);
-    const uint64_t Tprev = T;
-    T += q;
-    const int n = i + 1;
-    const double th = (double)T * 0x1p-32 * (double)sps[R + n - 1];
-    const double th_prev = (n == 1) ? 0.0 : (double)Tprev * 0x1p-32 * (double)sps[R + n - 2];
-    if (th < th_prev && n < fail) fail = n;
-    if (th > best) { best = th; best_n = n; }
+  uint64_t T = T0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = i0 + e;
+    if (i < N) {
+      const uint64_t Tprev = T;
+      T += key_fixed_point(key[e]);
+      const int n = i + 1;
+      const double th = (double)T * 0x1p-32 * (double)sps[R + n - 1];
+      const double th_prev = (n == 1) ? 0.0 : (double)Tprev * 0x1p-32 * (double)sps[R + n - 2];
+      if (th < th_prev && n < fail) fail = n;
+      if (th > best) { best = th; best_n = n; }
+    }
   }
   fail = sdv::wave_min_i(fail);
-  // argmax over the wave: larger Theta, then smaller n
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const double ob = __shfl_xor(best, o, 64);
@@ -156,48 +188,48 @@ __global__ __launch_bounds__(kThreads) void k_schedule(
     else if (mode == SD_SCHED_GLOBAL_ARGMAX) nstar = bn;
     else nstar = sdv::clampi(*cap_k, 0, N);
     s_nstar = nstar;
-  }
-  __syncthreads();
-  const int nstar = s_nstar;
-
-  // 5. outputs.  Theta_{n*} is recomputed from the prefix sum by the owner.
-  if (tid == 0) {
     if (batch_out) *batch_out = R + nstar;
     if (n_sel_out) *n_sel_out = nstar;
     if (theta_out && nstar == 0) *theta_out = 0.0;
   }
-  if (theta_out && nstar > 0) {
-    const int i = nstar - 1;
-    if (i >= i0 && i < i0 + seg) {
-      uint64_t Ti = excl + wave_tot[wave];
-      for (int ii = i0; ii <= i; ++ii) Ti += key_fixed_point(keys[ii]);
-      *theta_out = (double)Ti * 0x1p-32 * (double)sps[R + nstar - 1];
+  __syncthreads();
+  const int nstar = s_nstar;
+
+  // 5. Theta_{n*} from its owner; l_r = largest selected position of request
+  //    r (the selected set is prefix-closed), gathered through LDS.
+  if (theta_out && nstar > 0 && nstar - 1 >= i0 && nstar - 1 < i0 + E) {
+    uint64_t Ti = T0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (i0 + e <= nstar - 1) Ti += key_fixed_point(key[e]);
+    *theta_out = (double)Ti * 0x1p-32 * (double)sps[R + nstar - 1];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (i0 + e < nstar) {
+      const uint32_t lo = (uint32_t)key[e];
+      atomicMax(&ell_lds[lo >> 8], (int)(lo & 0xFF));
     }
   }
-  // l_r = #{j : key(r, j) <= the n*-th smallest key}; the survival products
-  // are recomputed with the same fp32 multiplies, so the keys are identical.
-  const uint64_t kstar = nstar > 0 ? keys[nstar - 1] : 0;
-  for (int r = tid; r < R; r += kThreads) {
-    int cnt = 0;
-    if (nstar > 0) {
-      const int g = gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
-      float a = 1.0f;
-      for (int j = 1; j <= g; ++j) {
-        a = a * conf[(size_t)r * gmax + (j - 1)];
-        if (make_key(a, r, j) <= kstar) cnt = j;
-        else break;
-      }
-    }
-    ell[r] = cnt;
-  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kThreads) ell[r] = ell_lds[r];
+}
+
+size_t sched_ws_bytes(int R, int gmax) {
+  return sdv_align256((size_t)(R * gmax > 0 ? R * gmax : 1) * sizeof(uint64_t));
 }
 
 }  // namespace
 
+extern "C" size_t sd_schedule_workspace_size(int R, int gamma_max) {
+  if (R < 0 || gamma_max < 0) return 0;
+  return sched_ws_bytes(R, gamma_max);
+}
+
 extern "C" int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r,
                            const float* conf, const float* sps, int sps_len, int mode,
                            const int32_t* cap_k, int32_t* ell, int32_t* batch, int32_t* n_sel,
-                           double* theta, float* surv) {
+                           double* theta, float* surv, void* workspace, size_t workspace_bytes) {
   if (R < 0 || gamma_max < 0) return SD_EINVAL;
   if (gamma_max > SD_MAX_GAMMA) return SD_EUNSUPPORTED;
   if ((long long)R * gamma_max > SD_MAX_SCHED_SLOTS) return SD_EUNSUPPORTED;
@@ -206,9 +238,33 @@ extern "C" int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32
   if (mode == SD_SCHED_CAPPED_TOPK && !cap_k) return SD_EINVAL;
   if (R > 0 && (!ell || !sps || (gamma_max > 0 && !conf))) return SD_EINVAL;
   if ((long long)sps_len < (long long)R * (1 + gamma_max)) return SD_ERANGE;
+  if (!workspace || workspace_bytes < sched_ws_bytes(R, gamma_max)) return SD_ERANGE;
+  if (((uintptr_t)workspace & 7) != 0) return SD_EINVAL;
+  uint64_t* sorted = (uint64_t*)workspace;
+  const int nslots = R * gamma_max;
+  if (nslots > 0) {
+    const size_t lds = (size_t)nslots * sizeof(uint64_t);
+    if (lds > 64 * 1024)
+      SDV_TRY_LAUNCH(hipFuncSetAttribute((const void*)k_sched_rank,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    SDV_TRY_LAUNCH(sdv::launch(k_sched_rank, dim3((nslots + kRankCand - 1) / kRankCand),
+                               dim3(kRankThreads), lds, stream, R, gamma_max, gamma_r, conf, surv,
+                               sorted));
+  }
   int npad = 1;
-  while (npad < R * gamma_max) npad <<= 1;
-  SDV_TRY_LAUNCH(sdv::launch(k_schedule, dim3(1), dim3(kThreads), 0, stream, R, gamma_max, gamma_r,
-                             conf, sps, mode, cap_k, ell, batch, n_sel, theta, surv, npad));
+  while (npad < nslots) npad <<= 1;
+  const int E = npad > kThreads ? npad / kThreads : 1;
+#define SDV_SELECT_LAUNCH(EV)                                                                   \
+  SDV_TRY_LAUNCH(sdv::launch(k_sched_select<EV>, dim3(1), dim3(kThreads), 0, stream, R, gamma_max, \
+                             gamma_r, sps, mode, cap_k, (const uint64_t*)sorted, ell, batch, n_sel, \
+                             theta))
+  switch (E) {
+    case 1: SDV_SELECT_LAUNCH(1); break;
+    case 2: SDV_SELECT_LAUNCH(2); break;
+    case 4: SDV_SELECT_LAUNCH(4); break;
+    case 8: SDV_SELECT_LAUNCH(8); break;
+    default: SDV_SELECT_LAUNCH(16); break;
+  }
+#undef SDV_SELECT_LAUNCH
   return SD_OK;
 }

@@ -11,27 +11,32 @@
 //
 // Kernels (one stream, no host synchronisation):
 //   k_row_partials    the bandwidth pass: every needed target and draft row is
-//                     streamed once with 16-byte loads; each wave leaves a
-//                     partial (max, sum 2^(x*c - ref)) per 16384-element chunk
-//   k_accept          one workgroup per request: combine partials into (m, Z),
-//                     run the accept tests for all positions at once, find the
-//                     first rejection, write accepted tokens, plan the draw
-//   k_residual_sums   per (request, chunk): sum of max(0, p - q) over the
-//                     rejected position's row pair (skipped for bonus draws)
+//                     streamed once with 16-byte non-temporal loads; each wave
+//                     leaves a partial (max, sum 2^(x*c - ref)) per
+//                     16384-element chunk.  No LDS, no barrier.
+//   k_accept          one workgroup per request: combine the partials into
+//                     (m, Z) per row, run every accept test at once, find the
+//                     first rejection, write the accepted tokens, plan the draw
+//   k_residual_sums   per (request, chunk) of a rejected request: sums of
+//                     max(0, p - q) over the rejected position's row pair
 //   k_sample          one workgroup per request: locate the chunk where the
-//                     inverse CDF crosses u * sum(w), rescan that chunk only
+//                     inverse CDF crosses u * sum(w) (bonus draws take their
+//                     chunk sums straight from the first pass), rescan it
 #include "sdv_common.h"
 #include "sdv_host.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / 64;
-constexpr int kChunk = 16384;                 // elements per work item
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 16384;  // elements per work item
+constexpr int kMaxChunks = SD_MAX_VOCAB / kChunk;
+constexpr int kMaxSlots = 2 * SD_MAX_GAMMA + 1;
+constexpr int kStagedParts = 4096;  // partials of one request staged in LDS
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct Plan {
-  int kind;        // 0: nothing to draw (failed request), 1: residual, 2: bonus / from p
+  int kind;        // 0: nothing to draw (failed request), 1: residual, 2: from p
   int n_acc;
   int st;          // status bits so far
   int tslot;       // target slot of the draw
@@ -42,12 +47,38 @@ struct Plan {
   double u;        // correction uniform
 };
 
+struct VerifyArgs {
+  const char* tgt;
+  const int32_t* tgt_row0;
+  const char* drf;
+  const int32_t* drf_row0;
+  const int32_t* draft_tokens;
+  const int32_t* ell;
+  const int64_t* pos0;
+  int32_t* n_accepted;
+  int32_t* out_tokens;
+  int32_t* status;
+  float* probe_probs;
+  float* row_stats;
+  float2* partial;  // [R][S][n_ch][kWaves]
+  Plan* plans;      // [R]
+  double* rsum;     // [R][n_ch][kWaves]
+  int64_t ld_bytes;
+  uint64_t seed;
+  float c;          // log2(e) / T
+  float inv_t;
+  int gmax;
+  int V;
+  int n_ch;
+};
+
 // 16-byte vector of logits -> floats.  bf16: 8 values, fp32: 4 values.
 template <bool BF16>
 struct Vec;
 template <>
 struct Vec<true> {
   static constexpr int kElems = 8;
+  static constexpr int kBytes = 2;
   static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
   __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
     x[0] = sdv::bf16lo(v.x); x[1] = sdv::bf16hi(v.x);
@@ -62,6 +93,7 @@ struct Vec<true> {
 template <>
 struct Vec<false> {
   static constexpr int kElems = 4;
+  static constexpr int kBytes = 4;
   static constexpr uint32_t kNegInfWord = 0xFF800000u;
   __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
     x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
@@ -76,57 +108,47 @@ struct Vec<false> {
 // (then every contribution is 2^-inf = 0, or NaN if a NaN was present).
 __device__ __forceinline__ float exp_ref(float m, float c) { return m == kNegInf ? 0.0f : m * c; }
 
-// slot -> row pointer for request r, or nullptr if the slot is outside the batch.
-__device__ __forceinline__ const char* slot_row(int slot, int r, int L, int gmax, const char* tgt,
-                                                const int32_t* tgt_row0, const char* drf,
-                                                const int32_t* drf_row0, int64_t ld_bytes,
-                                                int64_t* row_index) {
-  if (slot <= gmax) {
-    if (slot > L) return nullptr;
-    const int64_t row = (int64_t)tgt_row0[r] + slot;
-    if (row_index) *row_index = row;
-    return tgt + row * ld_bytes;
-  }
-  const int j = slot - gmax;
-  if (j > L) return nullptr;
-  const int64_t row = (int64_t)drf_row0[r] + (j - 1);
-  if (row_index) *row_index = row;
-  return drf + row * ld_bytes;
+__device__ __forceinline__ int row_status(float M, double Z) {
+  if (isnan(M) || isnan(Z) || M == __builtin_huge_valf()) return SD_ST_NONFINITE;
+  if (M == kNegInf) return SD_ST_ZERO_Z;
+  return 0;
+}
+
+__device__ __forceinline__ bool slot_in_batch(int slot, int gmax, int L) {
+  return slot <= gmax ? slot <= L : slot - gmax <= L;
 }
 
 // ---------------------------------------------------------------------------
 // The bandwidth pass.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_row_partials(
-    const char* __restrict__ tgt, const int32_t* __restrict__ tgt_row0,
-    const char* __restrict__ drf, const int32_t* __restrict__ drf_row0,
-    const int32_t* __restrict__ ell, int gmax, int V, int64_t ld_bytes, float c, int n_ch,
-    float2* __restrict__ partial) {
+__global__ __launch_bounds__(kThreads) void k_row_partials(VerifyArgs a) {
   using VT = Vec<BF16>;
-  constexpr int kVecPerThread = kChunk / VT::kElems / kThreads;
+  constexpr int kVec = kChunk / VT::kElems / kThreads;
   const int item = blockIdx.x;
-  const int S = 2 * gmax + 1;
-  const int ch = item % n_ch;
-  const int rs = item / n_ch;
+  const int S = 2 * a.gmax + 1;
+  const int ch = item % a.n_ch;
+  const int rs = item / a.n_ch;
   const int slot = rs % S, r = rs / S;
-  const int L = sdv::clampi(ell[r], 0, gmax);
-  const char* row = slot_row(slot, r, L, gmax, tgt, tgt_row0, drf, drf_row0, ld_bytes, nullptr);
-  if (!row) return;
-
+  const int L = sdv::clampi(a.ell[r], 0, a.gmax);
+  if (!slot_in_batch(slot, a.gmax, L)) return;
+  const char* row = slot <= a.gmax
+                        ? a.tgt + ((int64_t)a.tgt_row0[r] + slot) * a.ld_bytes
+                        : a.drf + ((int64_t)a.drf_row0[r] + (slot - a.gmax - 1)) * a.ld_bytes;
   const int e0 = ch * kChunk;
-  const int nvec = min(kChunk, V - e0) / VT::kElems;
-  const uint4* p = (const uint4*)(row + (int64_t)e0 * (BF16 ? 2 : 4));
+  const int nvec = min(kChunk, a.V - e0) / VT::kElems;
+  const uint4* p = (const uint4*)(row + (int64_t)e0 * VT::kBytes);
   const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  const float c = a.c;
 
-  uint4 buf[kVecPerThread];
+  uint4 buf[kVec];
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
+  for (int k = 0; k < kVec; ++k) {
     const int v = threadIdx.x + k * kThreads;
     buf[k] = v < nvec ? sdv::ld_nt(p + v) : ninf;
   }
   float m = kNegInf;
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
+  for (int k = 0; k < kVec; ++k) {
     float x[VT::kElems];
     VT::unpack(buf[k], x);
 #pragma unroll
@@ -135,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(
   const float ref = exp_ref(m, c);
   float s = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
+  for (int k = 0; k < kVec; ++k) {
     float x[VT::kElems];
     VT::unpack(buf[k], x);
 #pragma unroll
@@ -144,111 +166,104 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(
   // wave partial: rescale every lane to the wave max
   const float wm = sdv::wave_max(m);
   const float wref = exp_ref(wm, c);
-  const float contrib = (s == 0.0f) ? 0.0f : s * sdv::fast_exp2(ref - wref);
-  const float ws = sdv::wave_sum(contrib);
-  if ((threadIdx.x & 63) == 0) {
-    const int wave = threadIdx.x >> 6;
-    partial[((size_t)rs * n_ch + ch) * kWavesPerBlock + wave] = make_float2(wm, ws);
-  }
-}
-
-// Combine the partials of one row: M = max, ref = fp32(M * c),
-// Z = sum s_w 2^(ref_w - ref) in fp64.
-__device__ void combine_row(const float2* __restrict__ pp, int nparts, float c, float* M_out,
-                            float* ref_out, double* Z_out) {
-  float M = kNegInf;
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, pp[q].x);
-  const float ref = exp_ref(M, c);
-  double Z = 0.0;
-  for (int q = 0; q < nparts; ++q) {
-    const float s = pp[q].y;
-    if (s != 0.0f) Z += (double)s * exp2((double)exp_ref(pp[q].x, c) - (double)ref);
-  }
-  *M_out = M;
-  *ref_out = ref;
-  *Z_out = Z;
-}
-
-__device__ __forceinline__ int row_status(float M, double Z) {
-  if (isnan(M) || isnan(Z) || M == __builtin_huge_valf()) return SD_ST_NONFINITE;
-  if (M == kNegInf) return SD_ST_ZERO_Z;
-  return 0;
+  const float ws = sdv::wave_sum((s == 0.0f) ? 0.0f : s * sdv::fast_exp2(ref - wref));
+  if ((threadIdx.x & 63) == 0)
+    a.partial[((size_t)rs * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = make_float2(wm, ws);
 }
 
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_accept(
-    int gmax, int V, int64_t ld_bytes, float c, float inv_t, uint64_t seed,
-    const int64_t* __restrict__ pos0, const char* __restrict__ tgt,
-    const int32_t* __restrict__ tgt_row0, const char* __restrict__ drf,
-    const int32_t* __restrict__ drf_row0, const int32_t* __restrict__ draft_tokens,
-    const int32_t* __restrict__ ell, int n_ch, const float2* __restrict__ partial,
-    int32_t* __restrict__ n_accepted, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ status, float* __restrict__ probe_probs, float* __restrict__ row_stats,
-    Plan* __restrict__ plans) {
+__global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   using VT = Vec<BF16>;
-  __shared__ float sM[2 * SD_MAX_GAMMA + 1];
-  __shared__ float sRef[2 * SD_MAX_GAMMA + 1];
-  __shared__ double sZ[2 * SD_MAX_GAMMA + 1];
+  __shared__ float sM[kMaxSlots];
+  __shared__ float sRef[kMaxSlots];
+  __shared__ double sZ[kMaxSlots];
+  __shared__ float2 sPart[kStagedParts];
   __shared__ int s_st, s_jstar, s_zero_q_upto;
 
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const int S = 2 * gmax + 1;
-  const int L = sdv::clampi(ell[r], 0, gmax);
-  const int nparts = n_ch * kWavesPerBlock;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gmax = a.gmax, S = 2 * gmax + 1, V = a.V;
+  const int L = sdv::clampi(a.ell[r], 0, gmax);
+  const int nparts = a.n_ch * kWaves;
+  const float c = a.c;
   if (tid == 0) { s_st = 0; s_jstar = L + 1; s_zero_q_upto = 0x7FFFFFFF; }
-  __syncthreads();
 
-  for (int slot = tid; slot < S; slot += kThreads) {
-    const bool in_batch = slot <= gmax ? slot <= L : slot - gmax <= L;
-    if (!in_batch) continue;
-    float M, ref;
-    double Z;
-    combine_row(partial + (size_t)(r * S + slot) * nparts, nparts, c, &M, &ref, &Z);
-    sM[slot] = M;
-    sRef[slot] = ref;
-    sZ[slot] = Z;
-    const int st = row_status(M, Z);
-    if (st) atomicOr(&s_st, st);
-    if (row_stats) {
-      // report m = max(x)/T and Z = sum exp(x/T - m): shift Z from the fp32
-      // reference to the exact one.
-      const double zrep = Z * exp2((double)ref - (double)M * (double)c);
-      row_stats[((size_t)r * S + slot) * 2 + 0] = M * inv_t;
-      row_stats[((size_t)r * S + slot) * 2 + 1] = (float)zrep;
+  // Stage the partials of the batch rows (target slots 0..L, then draft slots
+  // gmax+1..gmax+L, i.e. local row b) in LDS when they fit: one load each.
+  const int nrows = 2 * L + 1;
+  const bool staged = (long long)nrows * nparts <= kStagedParts;
+  const float2* base = a.partial + (size_t)r * S * nparts;
+  if (staged) {
+    for (int i = tid; i < nrows * nparts; i += kThreads) {
+      const int b = i / nparts, q = i % nparts;
+      const int slot = b <= L ? b : gmax + (b - L);
+      sPart[i] = base[(size_t)slot * nparts + q];
     }
   }
   __syncthreads();
 
-  const int64_t pbase = pos0 ? pos0[r] : 0;
-  Plan* plan = plans + r;
+  // (m, Z) per row: wave w combines rows w, w+4, ..., lanes over the partials
+  for (int b = wave; b < nrows; b += kWaves) {
+    const int slot = b <= L ? b : gmax + (b - L);
+    const float2* pp = staged ? sPart + b * nparts : base + (size_t)slot * nparts;
+    float M = kNegInf;
+    for (int q = lane; q < nparts; q += 64) M = fmaxf(M, pp[q].x);
+    M = sdv::wave_max(M);
+    const float ref = exp_ref(M, c);
+    double Z = 0.0;
+    for (int q = lane; q < nparts; q += 64) {
+      const float2 v = pp[q];
+      if (v.y != 0.0f) Z += (double)v.y * exp2((double)exp_ref(v.x, c) - (double)ref);
+    }
+    Z = sdv::wave_sum_d(Z);
+    if (lane == 0) {
+      sM[slot] = M;
+      sRef[slot] = ref;
+      sZ[slot] = Z;
+      const int st = row_status(M, Z);
+      if (st) atomicOr(&s_st, st);
+      if (a.row_stats) {
+        // report m = max(x)/T and Z = sum exp(x/T - m): move Z from the fp32
+        // reference to the exact one
+        const double zrep = Z * exp2((double)ref - (double)M * (double)c);
+        a.row_stats[((size_t)r * S + slot) * 2 + 0] = M * a.inv_t;
+        a.row_stats[((size_t)r * S + slot) * 2 + 1] = (float)zrep;
+      }
+    }
+  }
+  __syncthreads();
+
+  Plan* plan = a.plans + r;
+  int32_t* out_tok = a.out_tokens + (size_t)r * (gmax + 1);
   if (s_st) {  // a needed row is unusable: the request fails
-    for (int t = tid; t <= gmax; t += kThreads) out_tokens[(size_t)r * (gmax + 1) + t] = -1;
+    for (int t = tid; t <= gmax; t += kThreads) out_tok[t] = -1;
     if (tid == 0) {
-      n_accepted[r] = 0;
-      status[r] = s_st;
+      a.n_accepted[r] = 0;
+      a.status[r] = s_st;
       plan->kind = 0;
     }
     return;
   }
 
-  // all accept tests in parallel; the chain stops at the first rejection
+  // every accept test at once; the chain stops at the first rejection
+  const int64_t pbase = a.pos0 ? a.pos0[r] : 0;
+  const int32_t* drafts = a.draft_tokens + (size_t)r * gmax;
   for (int j = tid + 1; j <= L; j += kThreads) {
-    const int x = draft_tokens[(size_t)r * gmax + (j - 1)];
+    const int x = drafts[j - 1];
     bool reject;
     if (x < 0 || x >= V) {
       reject = true;
     } else {
-      const char* trow = tgt + ((int64_t)tgt_row0[r] + (j - 1)) * ld_bytes;
-      const char* drow = drf + ((int64_t)drf_row0[r] + (j - 1)) * ld_bytes;
+      const char* trow = a.tgt + ((int64_t)a.tgt_row0[r] + (j - 1)) * a.ld_bytes;
+      const char* drow = a.drf + ((int64_t)a.drf_row0[r] + (j - 1)) * a.ld_bytes;
       const int ts = j - 1, ds = gmax + j;
       const double p = exp2((double)VT::at(trow, x) * (double)c - (double)sRef[ts]) / sZ[ts];
       const double q = exp2((double)VT::at(drow, x) * (double)c - (double)sRef[ds]) / sZ[ds];
-      if (probe_probs) {
-        probe_probs[((size_t)r * gmax + (j - 1)) * 2 + 0] = (float)p;
-        probe_probs[((size_t)r * gmax + (j - 1)) * 2 + 1] = (float)q;
+      if (a.probe_probs) {
+        a.probe_probs[((size_t)r * gmax + (j - 1)) * 2 + 0] = (float)p;
+        a.probe_probs[((size_t)r * gmax + (j - 1)) * 2 + 1] = (float)q;
       }
-      const double u = sdv::uniform24(seed, (uint64_t)r, (uint64_t)(pbase + j), 1);
+      const double u = sdv::uniform24(a.seed, (uint64_t)r, (uint64_t)(pbase + j), 1);
       if (q == 0.0) {
         atomicMin(&s_zero_q_upto, j);
         reject = !(p > 0.0);
@@ -263,32 +278,28 @@ __global__ __launch_bounds__(kThreads) void k_accept(
   const int jstar = s_jstar;
   const bool rejected = jstar <= L;
   const int n = rejected ? jstar - 1 : L;
-  for (int t = tid; t <= gmax; t += kThreads) {
-    int v = -1;
-    if (t < n) v = draft_tokens[(size_t)r * gmax + t];
-    out_tokens[(size_t)r * (gmax + 1) + t] = v;
-  }
+  for (int t = tid; t <= gmax; t += kThreads) out_tok[t] = (t < n) ? drafts[t] : -1;
   if (tid == 0) {
     int st = 0;
     if (s_zero_q_upto <= (rejected ? jstar : L)) st |= SD_ST_ZERO_Q;
     if (rejected) {
-      const int x = draft_tokens[(size_t)r * gmax + (jstar - 1)];
+      const int x = drafts[jstar - 1];
       if (x < 0 || x >= V) st |= SD_ST_BAD_TOKEN;
     }
-    n_accepted[r] = n;
-    status[r] = st;
+    a.n_accepted[r] = n;
+    a.status[r] = st;
     Plan pl;
     pl.n_acc = n;
     pl.st = st;
     const int pos = rejected ? jstar : L + 1;
-    pl.u = sdv::uniform24(seed, (uint64_t)r, (uint64_t)(pbase + pos), 2);
+    pl.u = sdv::uniform24(a.seed, (uint64_t)r, (uint64_t)(pbase + pos), 2);
     pl.tslot = pos - 1;
-    pl.trow = (int64_t)tgt_row0[r] + (pos - 1);
+    pl.trow = (int64_t)a.tgt_row0[r] + (pos - 1);
     pl.mct = sRef[pos - 1];
     pl.zt = sZ[pos - 1];
     if (rejected) {
       pl.kind = 1;
-      pl.drow = (int64_t)drf_row0[r] + (jstar - 1);
+      pl.drow = (int64_t)a.drf_row0[r] + (jstar - 1);
       pl.mcd = sRef[gmax + jstar];
       pl.zd = sZ[gmax + jstar];
     } else {
@@ -302,255 +313,231 @@ __global__ __launch_bounds__(kThreads) void k_accept(
 }
 
 // ---------------------------------------------------------------------------
-// Residual weights w = max(0, p - q), in fp64 from fp32 exponentials.  Thread t
-// always owns the same elements of a chunk (vectors t, t + 256, ...), summed in
-// the same order, so k_sample can rescan one chunk consistently.
-template <bool BF16>
-__device__ __forceinline__ double thread_chunk_weights(const char* trow, const char* drow,
-                                                       int e0, int nvec, float c, float mct,
-                                                       double izt, float mcd, double izd,
-                                                       int kind, double* w_out) {
-  using VT = Vec<BF16>;
-  constexpr int kVecPerThread = kChunk / VT::kElems / kThreads;
-  const uint4* tp = (const uint4*)(trow + (int64_t)e0 * (BF16 ? 2 : 4));
-  const uint4* dp = drow ? (const uint4*)(drow + (int64_t)e0 * (BF16 ? 2 : 4)) : nullptr;
-  double sum = 0.0;
-#pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
-    const int v = threadIdx.x + k * kThreads;
-    if (v < nvec) {
-      float xt[VT::kElems], xd[VT::kElems];
-      VT::unpack(tp[v], xt);
-      if (kind == 1) VT::unpack(dp[v], xd);
-#pragma unroll
-      for (int e = 0; e < VT::kElems; ++e) {
-        double w;
-        const double et = (double)sdv::fast_exp2(fmaf(xt[e], c, -mct));
-        if (kind == 1) {
-          const double ed = (double)sdv::fast_exp2(fmaf(xd[e], c, -mcd));
-          w = fmax(0.0, et * izt - ed * izd);
-        } else {
-          w = et;
-        }
-        if (w_out) w_out[k * VT::kElems + e] = w;
-        sum += w;
-      }
-    } else if (w_out) {
-#pragma unroll
-      for (int e = 0; e < VT::kElems; ++e) w_out[k * VT::kElems + e] = 0.0;
-    }
-  }
-  return sum;
+// Weight of element e of the correction draw: residual max(0, p - q)
+// (kind 1) or the unnormalised target law 2^(x*c - ref) (kind 2); fp64 from
+// fp32 exponentials.
+__device__ __forceinline__ double draw_weight(float xt, float xd, int kind, float c, float mct,
+                                              double izt, float mcd, double izd) {
+  const double et = (double)sdv::fast_exp2(fmaf(xt, c, -mct));
+  if (kind != 1) return et;
+  const double ed = (double)sdv::fast_exp2(fmaf(xd, c, -mcd));
+  return fmax(0.0, et * izt - ed * izd);
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_residual_sums(
-    const char* __restrict__ tgt, const char* __restrict__ drf, int V, int64_t ld_bytes, float c,
-    int n_ch, const Plan* __restrict__ plans, double* __restrict__ rsum) {
+__global__ __launch_bounds__(kThreads) void k_residual_sums(VerifyArgs a) {
   using VT = Vec<BF16>;
-  const int r = blockIdx.x / n_ch, ch = blockIdx.x % n_ch;
-  const Plan pl = plans[r];
+  constexpr int kVec = kChunk / VT::kElems / kThreads;
+  const int r = blockIdx.x / a.n_ch, ch = blockIdx.x % a.n_ch;
+  const Plan pl = a.plans[r];
   if (pl.kind != 1) return;
   const int e0 = ch * kChunk;
-  const int nvec = min(kChunk, V - e0) / VT::kElems;
-  const double s = thread_chunk_weights<BF16>(tgt + pl.trow * ld_bytes, drf + pl.drow * ld_bytes,
-                                              e0, nvec, c, pl.mct, 1.0 / pl.zt, pl.mcd,
-                                              1.0 / pl.zd, 1, nullptr);
-  __shared__ double ws[kWavesPerBlock];
-  const double t = sdv::wave_sum_d(s);
-  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = t;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int w = 0; w < kWavesPerBlock; ++w) tot += ws[w];
-    rsum[(size_t)r * n_ch + ch] = tot;
+  const int nvec = min(kChunk, a.V - e0) / VT::kElems;
+  const uint4* tp = (const uint4*)(a.tgt + pl.trow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
+  const uint4* dp = (const uint4*)(a.drf + pl.drow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
+  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  uint4 tv[kVec], dv[kVec];
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) {
+    const int v = threadIdx.x + k * kThreads;
+    tv[k] = v < nvec ? tp[v] : ninf;
+    dv[k] = v < nvec ? dp[v] : ninf;
   }
+  const double izt = 1.0 / pl.zt, izd = 1.0 / pl.zd;
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) {
+    float xt[VT::kElems], xd[VT::kElems];
+    VT::unpack(tv[k], xt);
+    VT::unpack(dv[k], xd);
+#pragma unroll
+    for (int e = 0; e < VT::kElems; ++e) acc += draw_weight(xt[e], xd[e], 1, a.c, pl.mct, izt, pl.mcd, izd);
+  }
+  acc = sdv::wave_sum_d(acc);
+  if ((threadIdx.x & 63) == 0) a.rsum[((size_t)r * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = acc;
 }
 
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_sample(
-    const char* __restrict__ tgt, const char* __restrict__ drf, int gmax, int V, int64_t ld_bytes,
-    float c, int n_ch, const float2* __restrict__ partial, const Plan* __restrict__ plans,
-    const double* __restrict__ rsum, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ status) {
+__global__ __launch_bounds__(kThreads) void k_sample(VerifyArgs a) {
   using VT = Vec<BF16>;
-  constexpr int kVecPerThread = kChunk / VT::kElems / kThreads;
-  constexpr int kPerThread = kVecPerThread * VT::kElems;
-  __shared__ double s_chunk[SD_MAX_VOCAB / kChunk];
-  __shared__ int s_ch, s_last_pos;
+  constexpr int kQuarterVec = kChunk / VT::kElems / kWaves;  // vectors per wave
+  constexpr int kPerLane = kQuarterVec / 64;                  // vectors per lane
+  __shared__ double s_chunk[kMaxChunks];
+  __shared__ double s_wave_tot[kWaves];
+  __shared__ int s_ch, s_found, s_last, s_kind;
   __shared__ double s_target;
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const Plan pl = plans[r];
+  const Plan pl = a.plans[r];
   if (pl.kind == 0) return;
-  const int S = 2 * gmax + 1;
-  int kind = pl.kind;
+  const int S = 2 * a.gmax + 1, n_ch = a.n_ch, V = a.V;
+  const float c = a.c;
   int st = pl.st;
 
   // chunk sums of the weights
-  if (kind == 1) {
-    for (int ch = tid; ch < n_ch; ch += kThreads) s_chunk[ch] = rsum[(size_t)r * n_ch + ch];
+  if (pl.kind == 1) {
+    for (int ch = tid; ch < n_ch; ch += kThreads) {
+      const double* q = a.rsum + ((size_t)r * n_ch + ch) * kWaves;
+      s_chunk[ch] = (q[0] + q[1]) + (q[2] + q[3]);
+    }
     __syncthreads();
     if (tid == 0) {
       double tot = 0.0;
       for (int ch = 0; ch < n_ch; ++ch) tot += s_chunk[ch];
-      s_target = tot;
+      s_kind = (tot > 0.0) ? 1 : 2;  // empty residual: draw from p_j* instead
     }
-    __syncthreads();
-    if (!(s_target > 0.0)) {  // empty residual: draw from p instead
-      kind = 2;
-      st |= SD_ST_ZERO_RESIDUAL;
-    }
-    __syncthreads();
-  }
-  if (kind == 2) {
-    // sum over chunk ch of 2^(x*c - mct), from the first pass's wave partials
-    const float2* pp = partial + (size_t)(r * S + pl.tslot) * n_ch * kWavesPerBlock;
-    for (int ch = tid; ch < n_ch; ch += kThreads) {
-      double s = 0.0;
-      for (int w = 0; w < kWavesPerBlock; ++w) {
-        const float2 q = pp[ch * kWavesPerBlock + w];
-        if (q.y != 0.0f) s += (double)q.y * exp2((double)exp_ref(q.x, c) - (double)pl.mct);
-      }
-      s_chunk[ch] = s;
-    }
+  } else if (tid == 0) {
+    s_kind = 2;
   }
   __syncthreads();
+  const int kind = s_kind;
+  if (pl.kind == 1 && kind == 2) st |= SD_ST_ZERO_RESIDUAL;
+  if (kind == 2) {  // sum over chunk ch of 2^(x*c - mct), from the first pass
+    const float2* pp = a.partial + ((size_t)r * S + pl.tslot) * n_ch * kWaves;
+    for (int ch = tid; ch < n_ch; ch += kThreads) {
+      double sum = 0.0;
+      for (int w = 0; w < kWaves; ++w) {
+        const float2 q = pp[ch * kWaves + w];
+        if (q.y != 0.0f) sum += (double)q.y * exp2((double)exp_ref(q.x, c) - (double)pl.mct);
+      }
+      s_chunk[ch] = sum;
+    }
+    __syncthreads();
+  }
   if (tid == 0) {
     double tot = 0.0;
     for (int ch = 0; ch < n_ch; ++ch) tot += s_chunk[ch];
     const double target = pl.u * tot;
-    double base = 0.0;
+    double acc = 0.0;
     int found = -1, last_pos = -1;
     for (int ch = 0; ch < n_ch; ++ch) {
       if (s_chunk[ch] > 0.0) last_pos = ch;
-      if (found < 0 && base + s_chunk[ch] > target) found = ch;
-      if (found < 0) base += s_chunk[ch];
+      if (found < 0 && acc + s_chunk[ch] > target) found = ch;
+      if (found < 0) acc += s_chunk[ch];
     }
     if (found < 0) {  // rounding put the target past the end: take the last mass
       found = last_pos;
       s_target = __builtin_huge_val();
     } else {
-      s_target = target - base;
+      s_target = target - acc;
     }
     s_ch = found;
-    s_last_pos = -1;
+    s_found = 0x7FFFFFFF;
+    s_last = -1;
   }
   __syncthreads();
   const int ch = s_ch;
-  const double target = s_target;
-  if (ch < 0) {  // no mass anywhere (cannot happen for a finite row)
+  int32_t* out_tok = a.out_tokens + (size_t)r * (a.gmax + 1);
+  if (ch < 0) {  // no mass anywhere (not reachable for a finite row)
     if (tid == 0) {
-      out_tokens[(size_t)r * (gmax + 1) + pl.n_acc] = -1;
-      status[r] = st;
+      out_tok[pl.n_acc] = -1;
+      a.status[r] = st;
     }
     return;
   }
 
-  // Rescan the located chunk.  Vocabulary order inside a chunk is
-  // (vector column k, thread, element): thread t owns vectors t, t+256, ...,
-  // so the cumulative sum is built column by column.
+  // Rescan the chunk: wave w owns the contiguous quarter
+  // [w*kQuarterVec, (w+1)*kQuarterVec) of its vectors, lane l the vectors
+  // w*kQuarterVec + k*64 + l; vocabulary order is (k, lane, element).
+  const double target = s_target;
   const int e0 = ch * kChunk;
   const int nvec = min(kChunk, V - e0) / VT::kElems;
-  double w[kPerThread];
-  const char* trow = tgt + pl.trow * ld_bytes;
-  const char* drow = kind == 1 ? drf + pl.drow * ld_bytes : nullptr;
-  thread_chunk_weights<BF16>(trow, drow, e0, nvec, c, pl.mct, 1.0 / pl.zt, pl.mcd, 1.0 / pl.zd,
-                             kind, w);
-  __shared__ double s_col_tot[kWavesPerBlock];
-  __shared__ int s_found;
+  const uint4* tp = (const uint4*)(a.tgt + pl.trow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
+  const uint4* dp = kind == 1 ? (const uint4*)(a.drf + pl.drow * a.ld_bytes + (int64_t)e0 * VT::kBytes)
+                              : nullptr;
+  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  const double izt = 1.0 / pl.zt, izd = 1.0 / pl.zd;
+  uint4 tv[kPerLane], dv[kPerLane];
+#pragma unroll
+  for (int k = 0; k < kPerLane; ++k) {
+    const int v = wave * kQuarterVec + k * 64 + lane;
+    tv[k] = v < nvec ? tp[v] : ninf;
+    dv[k] = (v < nvec && dp) ? dp[v] : ninf;
+  }
+  double col[kPerLane];
+  double my_tot = 0.0;
   int last = -1;
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k)
-#pragma unroll
-    for (int e = 0; e < VT::kElems; ++e)
-      if (w[k * VT::kElems + e] > 0.0) last = e0 + (tid + k * kThreads) * VT::kElems + e;
-  if (tid == 0) s_found = 0x7FFFFFFF;
-  __syncthreads();
-  double run = 0.0;  // mass of all earlier columns
-  for (int k = 0; k < kVecPerThread; ++k) {
+  for (int k = 0; k < kPerLane; ++k) {
+    float xt[VT::kElems], xd[VT::kElems];
+    VT::unpack(tv[k], xt);
+    VT::unpack(dv[k], xd);
     double vs = 0.0;
 #pragma unroll
-    for (int e = 0; e < VT::kElems; ++e) vs += w[k * VT::kElems + e];
-    const double vincl = sdv::wave_incl_scan_d(vs, lane);
-    if (lane == 63) s_col_tot[wave] = vincl;
-    __syncthreads();
-    double vexcl = vincl - vs;
-    double coltot = 0.0;
-    for (int ww = 0; ww < kWavesPerBlock; ++ww) {
-      if (ww < wave) vexcl += s_col_tot[ww];
-      coltot += s_col_tot[ww];
+    for (int e = 0; e < VT::kElems; ++e) {
+      const double w = draw_weight(xt[e], xd[e], kind, c, pl.mct, izt, pl.mcd, izd);
+      vs += w;
+      if (w > 0.0) last = e0 + (wave * kQuarterVec + k * 64 + lane) * VT::kElems + e;
     }
-    const double c0 = run + vexcl;
-    if (c0 <= target && c0 + vs > target) {
-      double cc = c0;
-      for (int e = 0; e < VT::kElems; ++e) {
-        cc += w[k * VT::kElems + e];
-        if (cc > target) {
-          atomicMin(&s_found, e0 + (tid + k * kThreads) * VT::kElems + e);
-          break;
+    col[k] = vs;
+    my_tot += vs;
+  }
+  const double wtot = sdv::wave_sum_d(my_tot);
+  if (lane == 0) s_wave_tot[wave] = wtot;
+  if (last >= 0) atomicMax(&s_last, last);
+  __syncthreads();
+  double run = 0.0;
+  for (int w = 0; w < wave; ++w) run += s_wave_tot[w];
+  if (run <= target && run + s_wave_tot[wave] > target) {
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+      const double incl = sdv::wave_incl_scan_d(col[k], lane);
+      const double c0 = run + (incl - col[k]);
+      int hit = 0x7FFFFFFF;
+      if (c0 <= target && c0 + col[k] > target) {
+        float xt[VT::kElems], xd[VT::kElems];
+        VT::unpack(tv[k], xt);
+        VT::unpack(dv[k], xd);
+        double cc = c0;
+        for (int e = 0; e < VT::kElems; ++e) {
+          cc += draw_weight(xt[e], xd[e], kind, c, pl.mct, izt, pl.mcd, izd);
+          if (cc > target) {
+            hit = e0 + (wave * kQuarterVec + k * 64 + lane) * VT::kElems + e;
+            break;
+          }
         }
       }
+      hit = sdv::wave_min_i(hit);
+      if (hit != 0x7FFFFFFF) {
+        if (lane == 0) atomicMin(&s_found, hit);
+        break;
+      }
+      run += __shfl(incl, 63, 64);
     }
-    run += coltot;
-    __syncthreads();
   }
-  if (last >= 0) atomicMax(&s_last_pos, last);
   __syncthreads();
   if (tid == 0) {
     int token = s_found;
-    if (token == 0x7FFFFFFF) token = s_last_pos;  // rounding: last element with mass
-    out_tokens[(size_t)r * (gmax + 1) + pl.n_acc] = token;
-    status[r] = st;
+    if (token == 0x7FFFFFFF) token = s_last;  // rounding: last element with mass
+    out_tok[pl.n_acc] = token;
+    a.status[r] = st;
   }
 }
 
-template <bool BF16>
-int run_verify(hipStream_t stream, int R, int gmax, int V, int ld, float temperature,
-               uint64_t seed, const int64_t* pos0, const void* tgt, const int32_t* tgt_row0,
-               const void* drf, const int32_t* drf_row0, const int32_t* draft_tokens,
-               const int32_t* ell, int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
-               float* probe_probs, float* row_stats, void* ws, hipEvent_t ev0, hipEvent_t ev1) {
-  const int n_ch = (V + kChunk - 1) / kChunk;
-  const int S = 2 * gmax + 1;
-  const int64_t ld_bytes = (int64_t)ld * (BF16 ? 2 : 4);
-  const float c = sdv::kLog2e / temperature;
-  const float inv_t = 1.0f / temperature;
-  char* p = (char*)ws;
-  float2* partial = (float2*)p;
-  p += sdv_align256((size_t)R * S * n_ch * kWavesPerBlock * sizeof(float2));
-  Plan* plans = (Plan*)p;
-  p += sdv_align256((size_t)R * sizeof(Plan));
-  double* rsum = (double*)p;
-
-  const long long items = (long long)R * S * n_ch;
-  const bool timed = ev0 && ev1;
-  if (timed) SDV_TRY_LAUNCH(hipEventRecord(ev0, stream));
-  SDV_TRY_LAUNCH(sdv::launch(k_row_partials<BF16>, dim3((unsigned)items), dim3(kThreads), 0,
-                             stream, (const char*)tgt, tgt_row0, (const char*)drf, drf_row0, ell,
-                             gmax, V, ld_bytes, c, n_ch, partial));
-  if (timed) SDV_TRY_LAUNCH(hipEventRecord(ev1, stream));
-  SDV_TRY_LAUNCH(sdv::launch(k_accept<BF16>, dim3(R), dim3(kThreads), 0, stream, gmax, V,
-                             ld_bytes, c, inv_t, seed, pos0, (const char*)tgt, tgt_row0,
-                             (const char*)drf, drf_row0, draft_tokens, ell, n_ch,
-                             (const float2*)partial, n_accepted, out_tokens, status, probe_probs,
-                             row_stats, plans));
-  SDV_TRY_LAUNCH(sdv::launch(k_residual_sums<BF16>, dim3((unsigned)(R * n_ch)), dim3(kThreads),
-                             0, stream, (const char*)tgt, (const char*)drf, V, ld_bytes, c, n_ch,
-                             (const Plan*)plans, rsum));
-  SDV_TRY_LAUNCH(sdv::launch(k_sample<BF16>, dim3(R), dim3(kThreads), 0, stream,
-                             (const char*)tgt, (const char*)drf, gmax, V, ld_bytes, c, n_ch,
-                             (const float2*)partial, (const Plan*)plans, (const double*)rsum,
-                             out_tokens, status));
-  return SD_OK;
+size_t partial_bytes(int R, int gmax, int V) {
+  const size_t n_ch = ((size_t)V + kChunk - 1) / kChunk;
+  return sdv_align256((size_t)R * (2 * (size_t)gmax + 1) * n_ch * kWaves * sizeof(float2));
 }
 
 size_t verify_ws_bytes(int R, int gmax, int V) {
   const size_t n_ch = ((size_t)V + kChunk - 1) / kChunk;
-  const size_t S = 2 * (size_t)gmax + 1;
-  return sdv_align256((size_t)R * S * n_ch * kWavesPerBlock * sizeof(float2)) +
-         sdv_align256((size_t)R * sizeof(Plan)) + sdv_align256((size_t)R * n_ch * sizeof(double));
+  return partial_bytes(R, gmax, V) + sdv_align256((size_t)R * sizeof(Plan)) +
+         sdv_align256((size_t)R * n_ch * kWaves * sizeof(double));
+}
+
+template <bool BF16>
+int launch_verify(hipStream_t stream, int R, const VerifyArgs& a, long long items,
+                  hipEvent_t ev0, hipEvent_t ev1) {
+  const bool timed = ev0 && ev1;
+  if (timed) SDV_TRY_LAUNCH(hipEventRecord(ev0, stream));
+  SDV_TRY_LAUNCH(sdv::launch(k_row_partials<BF16>, dim3((unsigned)items), dim3(kThreads), 0, stream, a));
+  if (timed) SDV_TRY_LAUNCH(hipEventRecord(ev1, stream));
+  SDV_TRY_LAUNCH(sdv::launch(k_accept<BF16>, dim3(R), dim3(kThreads), 0, stream, a));
+  SDV_TRY_LAUNCH(sdv::launch(k_residual_sums<BF16>, dim3((unsigned)(R * a.n_ch)), dim3(kThreads), 0,
+                             stream, a));
+  SDV_TRY_LAUNCH(sdv::launch(k_sample<BF16>, dim3(R), dim3(kThreads), 0, stream, a));
+  return SD_OK;
 }
 
 }  // namespace
@@ -579,15 +566,36 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
   if ((((uintptr_t)tgt_logits) & 15) != 0 || (drf_logits && (((uintptr_t)drf_logits) & 15) != 0))
     return SD_EINVAL;
-  const long long items = (long long)R * (2 * gamma_max + 1) * ((V + kChunk - 1) / kChunk);
+  const int n_ch = (V + kChunk - 1) / kChunk;
+  const long long items = (long long)R * (2 * gamma_max + 1) * n_ch;
   if (items > 0x7FFFFFFFLL) return SD_EUNSUPPORTED;
-  if (dtype == SD_DTYPE_BF16)
-    return run_verify<true>(stream, R, gamma_max, V, ld, temperature, seed, pos0, tgt_logits,
-                            tgt_row0, drf_logits, drf_row0, draft_tokens, ell, n_accepted,
-                            out_tokens, status, probe_probs, row_stats, workspace, prof_start,
-                            prof_stop);
-  return run_verify<false>(stream, R, gamma_max, V, ld, temperature, seed, pos0, tgt_logits,
-                           tgt_row0, drf_logits, drf_row0, draft_tokens, ell, n_accepted,
-                           out_tokens, status, probe_probs, row_stats, workspace, prof_start,
-                           prof_stop);
+
+  VerifyArgs a;
+  a.tgt = (const char*)tgt_logits;
+  a.tgt_row0 = tgt_row0;
+  a.drf = (const char*)(drf_logits ? drf_logits : tgt_logits);
+  a.drf_row0 = drf_row0;
+  a.draft_tokens = draft_tokens;
+  a.ell = ell;
+  a.pos0 = pos0;
+  a.n_accepted = n_accepted;
+  a.out_tokens = out_tokens;
+  a.status = status;
+  a.probe_probs = probe_probs;
+  a.row_stats = row_stats;
+  char* p = (char*)workspace;
+  a.partial = (float2*)p;
+  p += partial_bytes(R, gamma_max, V);
+  a.plans = (Plan*)p;
+  p += sdv_align256((size_t)R * sizeof(Plan));
+  a.rsum = (double*)p;
+  a.ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
+  a.seed = seed;
+  a.c = sdv::kLog2e / temperature;
+  a.inv_t = 1.0f / temperature;
+  a.gmax = gamma_max;
+  a.V = V;
+  a.n_ch = n_ch;
+  if (dtype == SD_DTYPE_BF16) return launch_verify<true>(stream, R, a, items, prof_start, prof_stop);
+  return launch_verify<false>(stream, R, a, items, prof_start, prof_stop);
 }

@@ -124,12 +124,16 @@ const char* sd_status_string(int code);
  *   ell        [R] int32 out
  *   batch, n_sel  [1] int32 out or NULL;  theta [1] fp64 out (Theta_{n*}) or NULL
  *   surv       [R][gamma_max] fp32 out or NULL: a[r][j-1], 0 past gamma_r
- * Runs as one workgroup; nothing is read back to the host.
+ *   workspace  at least sd_schedule_workspace_size(R, gamma_max) bytes,
+ *              8-byte aligned (the sorted keys)
+ * Two launches (a chip-wide ranking pass, then one workgroup for the scan and
+ * the selection); nothing is read back to the host.
  */
+size_t sd_schedule_workspace_size(int R, int gamma_max);
 int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r,
                 const float* conf, const float* sps, int sps_len, int mode,
                 const int32_t* cap_k, int32_t* ell, int32_t* batch, int32_t* n_sel,
-                double* theta, float* surv);
+                double* theta, float* surv, void* workspace, size_t workspace_bytes);
 
 /*
  * sd_verify - lossless verification by rejection sampling [SD 1.1].

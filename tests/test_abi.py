@@ -46,10 +46,11 @@ def test_workspace_sizes():
 N = None
 
 
-def _sched(R, g, mode, sps_len, conf=1, sps=1, ell=1, cap=None):
+def _sched(R, g, mode, sps_len, conf=1, sps=1, ell=1, cap=None, ws=1 << 20):
     L = sdv.lib()
     p = lambda x: ctypes.c_void_p(16) if x else None
-    return L.sd_schedule(None, R, g, None, p(conf), p(sps), sps_len, mode, p(cap), p(ell), N, N, N, N)
+    return L.sd_schedule(None, R, g, None, p(conf), p(sps), sps_len, mode, p(cap), p(ell), N, N, N, N,
+                         ctypes.c_void_p(256), ws)
 
 
 def test_schedule_host_validation():
@@ -60,6 +61,7 @@ def test_schedule_host_validation():
     assert _sched(4, 4, 2, 100) == _lib.SD_EINVAL                  # capped without cap_k
     assert _sched(4, 4, 0, 19) == _lib.SD_ERANGE                   # table < R(1+g)
     assert _sched(4, 4, 0, 20, ell=0) == _lib.SD_EINVAL
+    assert _sched(4, 4, 0, 20, ws=64) == _lib.SD_ERANGE          # workspace < 16 keys
 
 
 def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=()):
