@@ -72,7 +72,7 @@ def lib():
     L.sd_verify_workspace_size.argtypes = [_I, _I, _I]
     L.sd_verify.restype = _I
     L.sd_verify.argtypes = [_P, _I, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P, _P,
-                            _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+                            _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
     L.sd_markov_draft_workspace_size.restype = _SZ
     L.sd_markov_draft_workspace_size.argtypes = [_I, _I, _I, _I]
     L.sd_markov_draft.restype = _I
@@ -155,11 +155,11 @@ def sd_verify_workspace_size(R, gmax, V):
 
 
 def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.0, seed=0,
-              pos0=None, probe=False, stats=False, workspace=None, out=None, stream=None,
-              prof_events=None):
+              pos0=None, probe=False, stats=False, alpha=False, workspace=None, out=None,
+              stream=None, prof_events=None):
     """Run verification.  tgt / drf: 2-D logit tensors (bf16 or fp32, ld =
     shape[1]); the rest int32 device tensors.  Returns a dict of device
-    tensors: n_acc, tokens, status (and probe, row_stats if asked).
+    tensors: n_acc, tokens, status (and probe, row_stats, alpha if asked).
     prof_events: optional pair of raw hipEvent_t handles (ints) recorded
     around the row-statistics pass."""
     R, gmax = draft_tokens.shape
@@ -179,6 +179,7 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
     status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
     pp = o.get("probe", torch.zeros((R, gmax, 2), dtype=torch.float32, device=dev)) if probe else None
     rs = o.get("row_stats", torch.zeros((R, 2 * gmax + 1, 2), dtype=torch.float32, device=dev)) if stats else None
+    al = o.get("alpha", torch.zeros((R, gmax), dtype=torch.float32, device=dev)) if alpha else None
     wsz = sd_verify_workspace_size(R, gmax, V)
     ws = workspace if workspace is not None else _workspace(wsz, dev)
     code = lib().sd_verify(
@@ -187,10 +188,11 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
         _ptr(drf, None, "drf"), _ptr(drf_row0, torch.int32, "drf_row0"),
         _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(ell, torch.int32, "ell"),
         _ptr(n_acc, torch.int32), _ptr(toks, torch.int32), _ptr(status, torch.int32),
-        _ptr(pp, torch.float32), _ptr(rs, torch.float32), ws.data_ptr(), ws.numel(),
+        _ptr(pp, torch.float32), _ptr(rs, torch.float32), _ptr(al, torch.float32),
+        ws.data_ptr(), ws.numel(),
         *(prof_events if prof_events else (None, None)))
     _check("sd_verify", code)
-    return dict(n_acc=n_acc, tokens=toks, status=status, probe=pp, row_stats=rs)
+    return dict(n_acc=n_acc, tokens=toks, status=status, probe=pp, row_stats=rs, alpha=al)
 
 
 def sd_markov_draft_workspace_size(R, gamma, V, rank):

@@ -52,10 +52,11 @@ __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, int lane) {
 }
 
 
-// Survival products of request r into keys[r*gmax .. r*gmax + gmax): fp32,
-// left to right; slots past gamma_r get the largest key.
-__device__ __forceinline__ int request_keys(int r, int gmax, const int32_t* gamma_r,
-                                            const float* conf, uint64_t* keys, float* surv) {
+// Survival products of request r, fp32 left to right: keys[i] holds conf[i]'s
+// bits on entry and the candidate's key on exit (slots past gamma_r get the
+// largest key).
+__device__ __forceinline__ void request_keys(int r, int gmax, const int32_t* gamma_r,
+                                             uint64_t* keys, float* surv) {
   const int g = gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
   float a = 1.0f;
   for (int j = 1; j <= gmax; ++j) {
@@ -63,14 +64,13 @@ __device__ __forceinline__ int request_keys(int r, int gmax, const int32_t* gamm
     uint64_t key = ~0ull;
     float out = 0.0f;
     if (j <= g) {
-      a = a * conf[i];
+      a = a * __uint_as_float((uint32_t)keys[i]);
       key = make_key(a, r, j);
       out = a;
     }
     keys[i] = key;
     if (surv) surv[i] = out;
   }
-  return g;
 }
 
 __global__ __launch_bounds__(kRankThreads) void k_sched_rank(
@@ -81,7 +81,9 @@ __global__ __launch_bounds__(kRankThreads) void k_sched_rank(
   const int tid = threadIdx.x;
   const int nslots = R * gmax;
   float* my_surv = blockIdx.x == 0 ? surv : nullptr;  // one workgroup writes it
-  for (int r = tid; r < R; r += kRankThreads) request_keys(r, gmax, gamma_r, conf, keys, my_surv);
+  for (int i = tid; i < nslots; i += kRankThreads) keys[i] = __float_as_uint(conf[i]);  // coalesced
+  __syncthreads();
+  for (int r = tid; r < R; r += kRankThreads) request_keys(r, gmax, gamma_r, keys, my_surv);
   __syncthreads();
   const int cl = tid % kRankCand, seg = tid / kRankCand;
   const int cand = blockIdx.x * kRankCand + cl;
@@ -89,7 +91,15 @@ __global__ __launch_bounds__(kRankThreads) void k_sched_rank(
   const int len = (nslots + kRankSegs - 1) / kRankSegs;
   const int i0 = seg * len, i1 = min(nslots, i0 + len);
   int cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += keys[i] < mine ? 1 : 0;
+  int i = i0;
+  for (; i + 8 <= i1; i += 8) {  // 8 independent LDS loads in flight
+    uint64_t q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = keys[i + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cnt += q[u] < mine ? 1 : 0;
+  }
+  for (; i < i1; ++i) cnt += keys[i] < mine ? 1 : 0;
   part[seg][cl] = cnt;
   __syncthreads();
   if (tid < kRankCand && mine != ~0ull) {
@@ -113,6 +123,19 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
   __shared__ int s_best_n[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nslots = R * gmax;
+  const int i0 = tid * E;
+  // issue the independent loads first: sorted keys (valid below N, known
+  // after the count) and the throughput table entries this thread needs
+  uint64_t key[E];
+  float sps_n[E], sps_prev;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = i0 + e;
+    key[e] = i < nslots ? sorted[i] : ~0ull;
+    sps_n[e] = i < nslots ? sps[R + i] : 0.0f;
+  }
+  sps_prev = (i0 >= 1 && i0 - 1 < nslots) ? sps[R + i0 - 1] : 0.0f;
   if (tid == 0) { s_count = 0; s_fail = 0x7FFFFFFF; }
   __syncthreads();
   int my_count = 0;
@@ -123,10 +146,9 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
   if (my_count) atomicAdd(&s_count, my_count);
   __syncthreads();
   const int N = s_count;
-  const int i0 = tid * E;
-  uint64_t key[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (i0 + e < N) ? sorted[i0 + e] : ~0ull;
+  for (int e = 0; e < E; ++e)
+    if (i0 + e >= N) key[e] = ~0ull;
 
   // 3. fixed-point tau scan over the sorted order.
   uint64_t my_sum = 0;
@@ -156,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
       const uint64_t Tprev = T;
       T += key_fixed_point(key[e]);
       const int n = i + 1;
-      const double th = (double)T * 0x1p-32 * (double)sps[R + n - 1];
-      const double th_prev = (n == 1) ? 0.0 : (double)Tprev * 0x1p-32 * (double)sps[R + n - 2];
+      const double th = (double)T * 0x1p-32 * (double)sps_n[e];
+      const double th_prev = (n == 1) ? 0.0 : (double)Tprev * 0x1p-32 * (double)(e == 0 ? sps_prev : sps_n[e - 1]);
       if (th < th_prev && n < fail) fail = n;
       if (th > best) { best = th; best_n = n; }
     }

@@ -22,6 +22,11 @@
 //   k_sample          one workgroup per request: locate the chunk where the
 //                     inverse CDF crosses u * sum(w) (bonus draws take their
 //                     chunk sums straight from the first pass), rescan it
+//   k_alpha_sums      only when the acceptance rates are asked for: per
+//                     (request, position, chunk), sums of min(p, q) - the
+//                     probability that the position is accepted, which is
+//                     1 - TV(p, q), the confidence label of the DSpark summary
+//                     ("2.1"); k_sample finishes the per-row totals
 #include "sdv_common.h"
 #include "sdv_host.h"
 
@@ -60,7 +65,11 @@ struct VerifyArgs {
   int32_t* status;
   float* probe_probs;
   float* row_stats;
+  float* accept_prob;  // [R][gmax] or null
   float2* partial;  // [R][S][n_ch][kWaves]
+  float* row_ref;   // [R][S] fp32(max * c) of every batch row
+  double* row_z;    // [R][S] sum 2^(x*c - ref)
+  double* asum;     // [R][gmax][n_ch][kWaves] chunk sums of min(p, q)
   Plan* plans;      // [R]
   double* rsum;     // [R][n_ch][kWaves]
   int64_t ld_bytes;
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   __shared__ float2 sPart[kStagedParts];
   __shared__ int s_st, s_jstar, s_zero_q_upto;
 
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int gmax = a.gmax, S = 2 * gmax + 1, V = a.V;
   const int L = sdv::clampi(a.ell[r], 0, gmax);
   const int nparts = a.n_ch * kWaves;
@@ -202,24 +211,29 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   }
   __syncthreads();
 
-  // (m, Z) per row: wave w combines rows w, w+4, ..., lanes over the partials
-  for (int b = wave; b < nrows; b += kWaves) {
+  // (m, Z) per row: 16 groups of 16 lanes, one row per group at a time
+  const int grp = tid >> 4, gl = tid & 15;
+  for (int b = grp; b < nrows; b += kThreads / 16) {
     const int slot = b <= L ? b : gmax + (b - L);
     const float2* pp = staged ? sPart + b * nparts : base + (size_t)slot * nparts;
     float M = kNegInf;
-    for (int q = lane; q < nparts; q += 64) M = fmaxf(M, pp[q].x);
-    M = sdv::wave_max(M);
+    for (int q = gl; q < nparts; q += 16) M = fmaxf(M, pp[q].x);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
     const float ref = exp_ref(M, c);
     double Z = 0.0;
-    for (int q = lane; q < nparts; q += 64) {
+    for (int q = gl; q < nparts; q += 16) {
       const float2 v = pp[q];
-      if (v.y != 0.0f) Z += (double)v.y * exp2((double)exp_ref(v.x, c) - (double)ref);
+      if (v.y != 0.0f) Z += (double)v.y * (double)sdv::fast_exp2(exp_ref(v.x, c) - ref);
     }
-    Z = sdv::wave_sum_d(Z);
-    if (lane == 0) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) Z += __shfl_xor(Z, o, 16);
+    if (gl == 0) {
       sM[slot] = M;
       sRef[slot] = ref;
       sZ[slot] = Z;
+      a.row_ref[(size_t)r * S + slot] = ref;
+      a.row_z[(size_t)r * S + slot] = Z;
       const int st = row_status(M, Z);
       if (st) atomicOr(&s_st, st);
       if (a.row_stats) {
@@ -336,25 +350,81 @@ __global__ __launch_bounds__(kThreads) void k_residual_sums(VerifyArgs a) {
   const uint4* tp = (const uint4*)(a.tgt + pl.trow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
   const uint4* dp = (const uint4*)(a.drf + pl.drow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
   const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
-  uint4 tv[kVec], dv[kVec];
-#pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    const int v = threadIdx.x + k * kThreads;
-    tv[k] = v < nvec ? tp[v] : ninf;
-    dv[k] = v < nvec ? dp[v] : ninf;
-  }
   const double izt = 1.0 / pl.zt, izd = 1.0 / pl.zd;
   double acc = 0.0;
+  // two halves of the thread's vectors keep the kernel within 64 VGPRs
+  constexpr int kHalf = kVec / 2;
 #pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    float xt[VT::kElems], xd[VT::kElems];
-    VT::unpack(tv[k], xt);
-    VT::unpack(dv[k], xd);
+  for (int h = 0; h < 2; ++h) {
+    uint4 tv[kHalf], dv[kHalf];
 #pragma unroll
-    for (int e = 0; e < VT::kElems; ++e) acc += draw_weight(xt[e], xd[e], 1, a.c, pl.mct, izt, pl.mcd, izd);
+    for (int k = 0; k < kHalf; ++k) {
+      const int v = threadIdx.x + (h * kHalf + k) * kThreads;
+      tv[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
+      dv[k] = v < nvec ? sdv::ld_nt(dp + v) : ninf;
+    }
+#pragma unroll
+    for (int k = 0; k < kHalf; ++k) {
+      float xt[VT::kElems], xd[VT::kElems];
+      VT::unpack(tv[k], xt);
+      VT::unpack(dv[k], xd);
+#pragma unroll
+      for (int e = 0; e < VT::kElems; ++e)
+        acc += draw_weight(xt[e], xd[e], 1, a.c, pl.mct, izt, pl.mcd, izd);
+    }
   }
   acc = sdv::wave_sum_d(acc);
   if ((threadIdx.x & 63) == 0) a.rsum[((size_t)r * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance rate of position j: sum over the vocabulary of min(p_j, q_j).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_alpha_sums(VerifyArgs a) {
+  using VT = Vec<BF16>;
+  constexpr int kVec = kChunk / VT::kElems / kThreads;
+  const int gmax = a.gmax, S = 2 * gmax + 1;
+  const int ch = blockIdx.x % a.n_ch;
+  const int rj = blockIdx.x / a.n_ch;
+  const int j = rj % gmax + 1, r = rj / gmax;
+  const int L = sdv::clampi(a.ell[r], 0, gmax);
+  if (j > L || a.plans[r].kind == 0) return;
+  const float mct = a.row_ref[(size_t)r * S + (j - 1)];
+  const float mcd = a.row_ref[(size_t)r * S + gmax + j];
+  const double izt = 1.0 / a.row_z[(size_t)r * S + (j - 1)];
+  const double izd = 1.0 / a.row_z[(size_t)r * S + gmax + j];
+  const int e0 = ch * kChunk;
+  const int nvec = min(kChunk, a.V - e0) / VT::kElems;
+  const uint4* tp = (const uint4*)(a.tgt + ((int64_t)a.tgt_row0[r] + (j - 1)) * a.ld_bytes + (int64_t)e0 * VT::kBytes);
+  const uint4* dp = (const uint4*)(a.drf + ((int64_t)a.drf_row0[r] + (j - 1)) * a.ld_bytes + (int64_t)e0 * VT::kBytes);
+  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  double acc = 0.0;
+  constexpr int kHalf = kVec / 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 tv[kHalf], dv[kHalf];
+#pragma unroll
+    for (int k = 0; k < kHalf; ++k) {
+      const int v = threadIdx.x + (h * kHalf + k) * kThreads;
+      tv[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
+      dv[k] = v < nvec ? sdv::ld_nt(dp + v) : ninf;
+    }
+#pragma unroll
+    for (int k = 0; k < kHalf; ++k) {
+      float xt[VT::kElems], xd[VT::kElems];
+      VT::unpack(tv[k], xt);
+      VT::unpack(dv[k], xd);
+#pragma unroll
+      for (int e = 0; e < VT::kElems; ++e) {
+        const double pt = (double)sdv::fast_exp2(fmaf(xt[e], a.c, -mct)) * izt;
+        const double qd = (double)sdv::fast_exp2(fmaf(xd[e], a.c, -mcd)) * izd;
+        acc += fmin(pt, qd);
+      }
+    }
+  }
+  acc = sdv::wave_sum_d(acc);
+  if ((threadIdx.x & 63) == 0)
+    a.asum[(((size_t)r * gmax + (j - 1)) * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -372,6 +442,17 @@ __global__ __launch_bounds__(kThreads) void k_sample(VerifyArgs a) {
   const Plan pl = a.plans[r];
   if (pl.kind == 0) return;
   const int S = 2 * a.gmax + 1, n_ch = a.n_ch, V = a.V;
+  if (a.accept_prob) {  // per-row totals of the min(p, q) chunk sums
+    const int L = sdv::clampi(a.ell[r], 0, a.gmax);
+    for (int j = tid + 1; j <= a.gmax; j += kThreads) {
+      double t = 0.0;
+      if (j <= L) {
+        const double* q = a.asum + ((size_t)r * a.gmax + (j - 1)) * n_ch * kWaves;
+        for (int i = 0; i < n_ch * kWaves; ++i) t += q[i];
+      }
+      a.accept_prob[(size_t)r * a.gmax + (j - 1)] = (float)t;
+    }
+  }
   const float c = a.c;
   int st = pl.st;
 
@@ -522,8 +603,11 @@ size_t partial_bytes(int R, int gmax, int V) {
 
 size_t verify_ws_bytes(int R, int gmax, int V) {
   const size_t n_ch = ((size_t)V + kChunk - 1) / kChunk;
+  const size_t S = 2 * (size_t)gmax + 1;
   return partial_bytes(R, gmax, V) + sdv_align256((size_t)R * sizeof(Plan)) +
-         sdv_align256((size_t)R * n_ch * kWaves * sizeof(double));
+         sdv_align256((size_t)R * n_ch * kWaves * sizeof(double)) +
+         sdv_align256((size_t)R * S * sizeof(float)) + sdv_align256((size_t)R * S * sizeof(double)) +
+         sdv_align256((size_t)R * gmax * n_ch * kWaves * sizeof(double));
 }
 
 template <bool BF16>
@@ -536,6 +620,9 @@ int launch_verify(hipStream_t stream, int R, const VerifyArgs& a, long long item
   SDV_TRY_LAUNCH(sdv::launch(k_accept<BF16>, dim3(R), dim3(kThreads), 0, stream, a));
   SDV_TRY_LAUNCH(sdv::launch(k_residual_sums<BF16>, dim3((unsigned)(R * a.n_ch)), dim3(kThreads), 0,
                              stream, a));
+  if (a.accept_prob && a.gmax > 0)
+    SDV_TRY_LAUNCH(sdv::launch(k_alpha_sums<BF16>, dim3((unsigned)((long long)R * a.gmax * a.n_ch)),
+                               dim3(kThreads), 0, stream, a));
   SDV_TRY_LAUNCH(sdv::launch(k_sample<BF16>, dim3(R), dim3(kThreads), 0, stream, a));
   return SD_OK;
 }
@@ -552,8 +639,9 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
                          const void* tgt_logits, const int32_t* tgt_row0, const void* drf_logits,
                          const int32_t* drf_row0, const int32_t* draft_tokens,
                          const int32_t* ell, int32_t* n_accepted, int32_t* out_tokens,
-                         int32_t* status, float* probe_probs, float* row_stats, void* workspace,
-                         size_t workspace_bytes, hipEvent_t prof_start, hipEvent_t prof_stop) {
+                         int32_t* status, float* probe_probs, float* row_stats,
+                         float* accept_prob, void* workspace, size_t workspace_bytes,
+                         hipEvent_t prof_start, hipEvent_t prof_stop) {
   if (R < 0 || gamma_max < 0 || V < 8 || (V % 8) != 0 || ld < V || (ld % 8) != 0) return SD_EINVAL;
   if (gamma_max > SD_MAX_GAMMA || V > SD_MAX_VOCAB) return SD_EUNSUPPORTED;
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_EINVAL;
@@ -583,12 +671,20 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   a.status = status;
   a.probe_probs = probe_probs;
   a.row_stats = row_stats;
+  a.accept_prob = accept_prob;
+  const size_t S = 2 * (size_t)gamma_max + 1;
   char* p = (char*)workspace;
   a.partial = (float2*)p;
   p += partial_bytes(R, gamma_max, V);
   a.plans = (Plan*)p;
   p += sdv_align256((size_t)R * sizeof(Plan));
   a.rsum = (double*)p;
+  p += sdv_align256((size_t)R * n_ch * kWaves * sizeof(double));
+  a.row_ref = (float*)p;
+  p += sdv_align256((size_t)R * S * sizeof(float));
+  a.row_z = (double*)p;
+  p += sdv_align256((size_t)R * S * sizeof(double));
+  a.asum = (double*)p;
   a.ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
   a.seed = seed;
   a.c = sdv::kLog2e / temperature;

@@ -170,6 +170,11 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *               Z = sum exp(row/T - m): slots 0..gamma_max are target rows of
  *               positions 1..gamma_max+1, slots gamma_max+1.. are draft rows of
  *               positions 1..gamma_max; only slots inside the batch are written
+ *   accept_prob [R][gamma_max] fp32 or NULL: alpha_j = sum_v min(p_j(v), q_j(v)),
+ *               the probability that position j is accepted given the prefix
+ *               was, i.e. 1 - TV(p_j, q_j), the label the confidence head is
+ *               trained on [DS 2.1]; 0 past ell.  Costs a second read of every
+ *               verified row pair (not done when NULL).
  * prof_start, prof_stop  optional HIP events (both or neither): recorded on
  *             `stream` right before and after the row-statistics pass (the
  *             bandwidth-bound kernel that streams every row once), so a caller
@@ -187,7 +192,7 @@ int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype
               const void* drf_logits, const int32_t* drf_row0,
               const int32_t* draft_tokens, const int32_t* ell,
               int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
-              float* probe_probs, float* row_stats,
+              float* probe_probs, float* row_stats, float* accept_prob,
               void* workspace, size_t workspace_bytes,
               hipEvent_t prof_start, hipEvent_t prof_stop);
 

@@ -105,3 +105,7 @@ def check_stats(gpu, ora, reqs, ell, gmax):
         assert_rel(rs[r, gmax + 1:gmax + 1 + L, 1], ora["drf_stats"][i, :L, 1], what=f"r{r} draft Z")
         ok = ora["probe"][i, :L, 1] > 0
         assert_rel(pr[r, :L][ok], ora["probe"][i, :L][ok], what=f"r{r} probe p,q")
+        if gpu.get("alpha") is not None:
+            al = to_np(gpu["alpha"])
+            assert_rel(al[r, :L], ora["alpha"][i, :L], what=f"r{r} alpha", atol=1e-7)
+            assert np.all(al[r, L:] == 0)

@@ -68,7 +68,7 @@ def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=()):
     L = sdv.lib()
     P = lambda name: None if name in nulls else ctypes.c_void_p(256)
     return L.sd_verify(None, R, g, V, ld, dt, T, 1, None, P("tgt"), P("t0"), P("drf"), P("d0"),
-                       P("toks"), P("ell"), P("nacc"), P("out"), P("st"), None, None,
+                       P("toks"), P("ell"), P("nacc"), P("out"), P("st"), None, None, None,
                        ctypes.c_void_p(ws_ptr), ws, None, None)
 
 

@@ -17,10 +17,10 @@ from tests.parity_util import (oracle_verify_subset, compare_verify, check_stats
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_verify(inp, ell_dev, probe=True, stats=True, **kw):
+def _gpu_verify(inp, ell_dev, probe=True, stats=True, alpha=True, **kw):
     out = sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
                         inp["draft_tokens"], ell_dev, inp["V"], inp["temperature"], inp["seed"],
-                        pos0=inp.get("pos0"), probe=probe, stats=stats, **kw)
+                        pos0=inp.get("pos0"), probe=probe, stats=stats, alpha=alpha, **kw)
     torch.cuda.synchronize()
     return out
 
@@ -146,7 +146,7 @@ def test_verify_repeatable():
     ell = torch.full((inp["R"],), inp["gmax"], dtype=torch.int32, device="cuda")
     a = _gpu_verify(inp, ell)
     b = _gpu_verify(inp, ell)
-    for k in ("n_acc", "tokens", "status", "probe", "row_stats"):
+    for k in ("n_acc", "tokens", "status", "probe", "row_stats", "alpha"):
         assert torch.equal(a[k], b[k]), k
 
 
