@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_partials_headline.json")
-KERNEL_SOURCE = os.path.join(ROOT, "draft_verification_amd", "csrc", "verify.hip")
+# the bandwidth pass and the headers it is built from
+KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_amd", "csrc", f)
+                  for f in ("row_partials.hip", "verify_common.h", "sdv_common.h")]
 
 
 class HipEvents:
@@ -65,8 +67,11 @@ class HipEvents:
 
 
 def source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(bytes_per_launch):
@@ -118,6 +123,37 @@ def cpu_baseline(inp, ell, budget_s=12.0):
     }
 
 
+def bench_early_stop(sdv, torch, sets, bufs, ws, sws, steps):
+    """The same step with the early-stop schedule, which ends the batch at the
+    first decline of the throughput estimate: verification of the block it
+    chooses (context for the full-block headline figure)."""
+    V = sets[0]["V"]
+
+    def step(i):
+        inp = sets[i % len(sets)]
+        so, vo = bufs[i % len(sets)]
+        sch = sdv.sd_schedule(inp["conf"], inp["sps"], sdv.SD_SCHED_EARLY_STOP, out=so, workspace=sws)
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                      sch["ell"], V, inp["temperature"], inp["seed"], workspace=ws, out=vo)
+
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    blocks = [int(b[0]["batch"].item()) for b in bufs]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    B = sum(blocks) / len(blocks)
+    return {"verify_rows": blocks, "us_per_step": round(ms * 1e3, 1),
+            "rows_per_s": round(B / (ms / 1e3), 1),
+            "note": "the chosen rows of both input sets fit in the 256 MB last-level cache"}
+
+
 def bench_markov(sdv, torch, steps, hip):
     from workloads import markov_config
     inp = markov_config(device="cuda")
@@ -159,6 +195,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-markov", action="store_true")
+    ap.add_argument("--no-early-stop", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device three times (the known-size kernel that "
+                         "scales the rocprofv3 byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and has no "
@@ -175,6 +215,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = "cuda"
+    if args.copy_calibration:
+        n = 1 << 30
+        x = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+        return
     print("generating inputs", file=sys.stderr, flush=True)
     sets = [verify_config("headline", device=dev), verify_config("headline", device=dev, data_shift=1)]
     R, g, V = sets[0]["R"], sets[0]["gmax"], sets[0]["V"]
@@ -207,8 +256,6 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    batch = [int(b[0]["batch"].item()) for b in bufs]
-    assert all(b == R * (g + 1) for b in batch), batch
 
     K = args.steps
     kev = hip.create(2 * K)
@@ -225,6 +272,10 @@ def main():
     k_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(K)]
     hip.destroy(kev)
     ms_per_step = ms_total / K
+    # every input set that ran was scheduled as the full block
+    batch = [int(bufs[i][0]["batch"].item()) for i in range(min(args.warmup + K, len(sets)))]
+    assert all(b == R * (g + 1) for b in batch), batch
+    ell_full = bufs[0][0]["ell"].cpu().numpy()
     rows = R * (g + 1)
     value = rows * K / (ms_total / 1e3)
 
@@ -242,22 +293,48 @@ def main():
                                 workspace=sws)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
+    graph.replay()   # the first replay uploads the graph
+    torch.cuda.synchronize()
     s0 = torch.cuda.Event(enable_timing=True)
     s1 = torch.cuda.Event(enable_timing=True)
     s0.record()
-    for _ in range(5):
+    for _ in range(10):
         graph.replay()
     s1.record()
     torch.cuda.synchronize()
-    sched_us = s0.elapsed_time(s1) / 50 * 1e3
+    sched_us = s0.elapsed_time(s1) / 100 * 1e3
 
+    # practical read ceiling: a plain streaming read of a buffer of the batch's
+    # size with the bandwidth pass's load shape (two buffers alternate)
     bytes_launch = headline_bytes(R, g, V)
+    rbufs = [torch.empty(bytes_launch, dtype=torch.uint8, device=dev)
+             for _ in range(2)]
+    sink = torch.empty(max(sdv.lib().sd_stream_read_sink_words(bytes_launch), 1), dtype=torch.int32,
+                       device=dev)
+    for i in range(4):
+        sdv.sd_stream_read(rbufs[i % 2], sink=sink)
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for i in range(20):
+        sdv.sd_stream_read(rbufs[i % 2], sink=sink)
+    r1.record()
+    torch.cuda.synchronize()
+    read_us = r0.elapsed_time(r1) / 20 * 1e3
+    del rbufs
+    read_gbs = bytes_launch / (read_us / 1e6) / 1e9
     k_avg = float(np.mean(k_ms))
     achieved = bytes_launch / (k_avg / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(bytes_launch),
                 "kernel": "k_row_partials<bf16>", "kernel_avg_us": round(k_avg * 1e3, 2),
-                "bytes_per_launch": bytes_launch}
+                "kernel_us_p10_p50_p90": [round(float(np.percentile(k_ms, q)) * 1e3, 1)
+                                          for q in (10, 50, 90)],
+                "bytes_per_launch": bytes_launch,
+                "read_ceiling": {"GBps": round(read_gbs, 1), "frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+                                 "kernel_frac_of_ceiling": round(achieved / read_gbs, 4),
+                                 "what": "plain streaming read of the same byte count, same load shape"}}
 
     result = {
         "metric": "verify rows/s at R=256,γ=11,V=151936 bf16; % of HBM roofline",
@@ -280,13 +357,15 @@ def main():
         "breakdown_us": {"step": round(ms_per_step * 1e3, 1), "schedule": round(sched_us, 1),
                          "row_stats_kernel": round(k_avg * 1e3, 1)},
     }
+    if not args.no_early_stop:
+        print("early-stop schedule", file=sys.stderr, flush=True)
+        result["early_stop_block"] = bench_early_stop(sdv, torch, sets, bufs, ws, sws, K)
     if not args.no_markov:
         print("markov head", file=sys.stderr, flush=True)
         result["markov_draft"] = bench_markov(sdv, torch, K, hip)
     if not args.no_cpu_baseline:
         print("cpu baseline (oracle)", file=sys.stderr, flush=True)
-        ell = bufs[0][0]["ell"].cpu().numpy()
-        result["cpu_baseline"] = cpu_baseline(sets[0], ell)
+        result["cpu_baseline"] = cpu_baseline(sets[0], ell_full)
     print(json.dumps(result))
 
 

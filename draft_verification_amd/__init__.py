@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     sd_verify_workspace_size,
     sd_markov_draft,
     sd_markov_draft_workspace_size,
+    sd_stream_read,
     SD_SCHED_EARLY_STOP,
     SD_SCHED_GLOBAL_ARGMAX,
     SD_SCHED_CAPPED_TOPK,

@@ -37,6 +37,7 @@ EXPORTS = (
     "sd_abi_version", "sd_status_string", "sd_schedule_workspace_size", "sd_schedule",
     "sd_verify_workspace_size",
     "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
+    "sd_stream_read_sink_words", "sd_stream_read",
 )
 
 
@@ -78,6 +79,10 @@ def lib():
     L.sd_markov_draft.restype = _I
     L.sd_markov_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P,
                                   _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
+    L.sd_stream_read_sink_words.restype = ctypes.c_longlong
+    L.sd_stream_read_sink_words.argtypes = [ctypes.c_longlong]
+    L.sd_stream_read.restype = _I
+    L.sd_stream_read.argtypes = [_P, _P, ctypes.c_longlong, _P]
     _lib = L
     return L
 
@@ -224,3 +229,18 @@ def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, w
         _ptr(status, torch.int32), ws.data_ptr(), ws.numel())
     _check("sd_markov_draft", code)
     return dict(tokens=tokens, q_logits=ql, conf=conf, status=status)
+
+
+def sd_stream_read(src, sink=None, stream=None):
+    """Measurement aid: stream every byte of the contiguous GPU tensor `src`
+    with the bandwidth pass's load shape (see sd_stream_read in sdv.h).
+    Returns the sink tensor (one uint32 fold per workgroup, as int32)."""
+    nbytes = src.numel() * src.element_size()
+    words = lib().sd_stream_read_sink_words(nbytes)
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    elif sink.numel() < words:
+        raise ValueError(f"sink needs {words} words")
+    _check("sd_stream_read", lib().sd_stream_read(_stream(stream), _ptr(src, name="src"), nbytes,
+                                                  _ptr(sink, torch.int32, "sink")))
+    return sink

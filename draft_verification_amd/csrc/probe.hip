@@ -1,0 +1,49 @@
+// Measurement aid, not part of the method: a plain streaming read with the
+// same load shape as the bandwidth pass of sd_verify (256-thread workgroups,
+// eight 16-byte non-temporal loads per thread, 32 KB per workgroup).  Its
+// duration over a buffer of the batch's size is the practical HBM read
+// ceiling that the bandwidth pass is compared with.
+#include "sdv_common.h"
+#include "sdv_host.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPer = 8;
+constexpr long long kVecPerBlock = (long long)kThreads * kPer;
+
+__global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* __restrict__ src, long long n,
+                                                          uint32_t* sink) {
+  const long long base = (long long)blockIdx.x * kVecPerBlock;
+  uint4 v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const long long i = base + threadIdx.x + (long long)k * kThreads;
+    v[k] = i < n ? sdv::ld_nt(src + i) : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  if (threadIdx.x == 0) sink[blockIdx.x] = x;  // one word per workgroup (wave 0's fold)
+}
+
+}  // namespace
+
+extern "C" long long sd_stream_read_sink_words(long long bytes) {
+  if (bytes < 0) return -1;
+  return (bytes / 16 + kVecPerBlock - 1) / kVecPerBlock;
+}
+
+extern "C" int sd_stream_read(hipStream_t stream, const void* src, long long bytes, uint32_t* sink) {
+  if (bytes < 0 || (bytes % 16) != 0) return SD_EINVAL;
+  if (bytes == 0) return SD_OK;
+  if (!src || !sink || (((uintptr_t)src) & 15) != 0) return SD_EINVAL;
+  const long long n = bytes / 16;
+  const long long blocks = (n + kVecPerBlock - 1) / kVecPerBlock;
+  if (blocks > 0x7FFFFFFFLL) return SD_EUNSUPPORTED;
+  SDV_TRY_LAUNCH(sdv::launch(k_stream_read, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                             (const uint4*)src, n, sink));
+  return SD_OK;
+}

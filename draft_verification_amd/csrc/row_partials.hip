@@ -1,0 +1,83 @@
+// The bandwidth pass of sd_verify: row statistics of every verify-batch row.
+//
+// Verification needs p = softmax(target row / T) and q = softmax(draft row / T)
+// at the drafted tokens (speculative-decoding history page, "1.1 mechanism"),
+// so the normaliser of every target and draft row in the batch is required;
+// this is the one pass over the whole batch and it is bound by HBM.
+//
+// One 256-thread workgroup per (batch row, 16384-element chunk): each thread
+// issues all of its 16-byte non-temporal loads together, takes the max and
+// then sum 2^(x*c - fp32(max*c)) in registers, and each wave leaves one
+// partial (max, sum).  No LDS, no barrier.  Workgroups of rows outside the
+// scheduled batch exit at once.
+#include "sdv_host.h"
+#include "verify_common.h"
+
+namespace {
+
+using sdv::kChunk;
+using sdv::kNegInf;
+using sdv::kRowThreads;
+using sdv::kRowWaves;
+
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_row_partials(sdv::RowPassArgs a) {
+  using VT = sdv::Vec<BF16>;
+  constexpr int kVec = kChunk / VT::kElems / kRowThreads;
+  const int item = blockIdx.x;
+  const int S = 2 * a.gmax + 1;
+  const int ch = item % a.n_ch;
+  const int rs = item / a.n_ch;
+  const int slot = rs % S, r = rs / S;
+  const int L = sdv::clampi(a.ell[r], 0, a.gmax);
+  if (!sdv::slot_in_batch(slot, a.gmax, L)) return;
+  const char* row = slot <= a.gmax
+                        ? a.tgt + ((int64_t)a.tgt_row0[r] + slot) * a.ld_bytes
+                        : a.drf + ((int64_t)a.drf_row0[r] + (slot - a.gmax - 1)) * a.ld_bytes;
+  const int e0 = ch * kChunk;
+  const int nvec = min(kChunk, a.V - e0) / VT::kElems;
+  const uint4* p = (const uint4*)(row + (int64_t)e0 * VT::kBytes);
+  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  const float c = a.c;
+
+  uint4 buf[kVec];
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) {
+    const int v = threadIdx.x + k * kRowThreads;
+    buf[k] = v < nvec ? sdv::ld_nt(p + v) : ninf;
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) {
+    float x[VT::kElems];
+    VT::unpack(buf[k], x);
+#pragma unroll
+    for (int e = 0; e < VT::kElems; ++e) m = fmaxf(m, x[e]);
+  }
+  const float ref = sdv::exp_ref(m, c);
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) {
+    float x[VT::kElems];
+    VT::unpack(buf[k], x);
+#pragma unroll
+    for (int e = 0; e < VT::kElems; ++e) s += sdv::fast_exp2(fmaf(x[e], c, -ref));
+  }
+  // wave partial: rescale every lane to the wave max
+  const float wm = sdv::wave_max(m);
+  const float wref = sdv::exp_ref(wm, c);
+  const float ws = sdv::wave_sum((s == 0.0f) ? 0.0f : s * sdv::fast_exp2(ref - wref));
+  if ((threadIdx.x & 63) == 0)
+    a.partial[((size_t)rs * a.n_ch + ch) * kRowWaves + (threadIdx.x >> 6)] = make_float2(wm, ws);
+}
+
+}  // namespace
+
+namespace sdv {
+
+hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned items, hipStream_t stream) {
+  if (bf16) return launch(k_row_partials<true>, dim3(items), dim3(kRowThreads), 0, stream, a);
+  return launch(k_row_partials<false>, dim3(items), dim3(kRowThreads), 0, stream, a);
+}
+
+}  // namespace sdv

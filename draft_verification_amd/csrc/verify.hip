@@ -10,47 +10,43 @@
 // 1 + l_r target rows per request, DSpark summary "2.2").
 //
 // Kernels (one stream, no host synchronisation):
-//   k_row_partials    the bandwidth pass: every needed target and draft row is
-//                     streamed once with 16-byte non-temporal loads; each wave
-//                     leaves a partial (max, sum 2^(x*c - ref)) per
-//                     16384-element chunk.  No LDS, no barrier.
-//   k_accept          one workgroup per request: combine the partials into
-//                     (m, Z) per row, run every accept test at once, find the
-//                     first rejection, write the accepted tokens, plan the draw
-//   k_residual_sums   per (request, chunk) of a rejected request: sums of
-//                     max(0, p - q) over the rejected position's row pair
-//   k_sample          one workgroup per request: locate the chunk where the
-//                     inverse CDF crosses u * sum(w) (bonus draws take their
-//                     chunk sums straight from the first pass), rescan it
-//   k_alpha_sums      only when the acceptance rates are asked for: per
-//                     (request, position, chunk), sums of min(p, q) - the
-//                     probability that the position is accepted, which is
-//                     1 - TV(p, q), the confidence label of the DSpark summary
-//                     ("2.1"); k_sample finishes the per-row totals
-#include "sdv_common.h"
+//   k_row_partials  (row_partials.hip) the bandwidth pass: one partial
+//                   (max, sum 2^(x*c - ref)) per wave and 16384-element chunk
+//                   of every batch row
+//   k_finish        one 1024-thread workgroup per request does the rest:
+//                   combine the partials into (m, Z) per row, run every accept
+//                   test at once, find the first rejection, write the accepted
+//                   tokens; then the correction draw.  A rejection streams the
+//                   rejected row pair once (16 waves, next block's loads in
+//                   flight) for the sums of max(0, p - q) per 1024-element
+//                   block, locates the block where the inverse CDF crosses
+//                   u * sum(w) with a workgroup prefix sum, and one wave scans
+//                   that block.  A bonus draw locates its chunk from the first
+//                   pass's partials and rescans only that chunk.
+//   k_alpha_sums,   only when the acceptance rates are asked for: sums of
+//   k_alpha_total   min(p, q) per (request, position, chunk), then per row -
+//                   the probability that the position is accepted, which is
+//                   1 - TV(p, q), the confidence label of the DSpark summary
+//                   ("2.1")
 #include "sdv_host.h"
+#include "verify_common.h"
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 16384;  // elements per work item
-constexpr int kMaxChunks = SD_MAX_VOCAB / kChunk;
-constexpr int kMaxSlots = 2 * SD_MAX_GAMMA + 1;
-constexpr int kStagedParts = 4096;  // partials of one request staged in LDS
-constexpr float kNegInf = -__builtin_huge_valf();
+using sdv::kChunk;
+using sdv::kNegInf;
+using sdv::kRowWaves;
 
-struct Plan {
-  int kind;        // 0: nothing to draw (failed request), 1: residual, 2: from p
-  int n_acc;
-  int st;          // status bits so far
-  int tslot;       // target slot of the draw
-  int64_t trow;    // target row index
-  int64_t drow;    // draft row index (kind 1)
-  float mct, mcd;  // exponent references of the two rows (fp32(max * c))
-  double zt, zd;   // sums of 2^(x*c - ref) of the two rows
-  double u;        // correction uniform
-};
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kBlk = 1024;                          // elements per residual block
+constexpr int kChunkBlocks = kChunk / kBlk;         // = kFinWaves: one block per wave
+constexpr int kMaxSlots = 2 * SD_MAX_GAMMA + 1;
+constexpr int kStagedParts = 4096;                  // partials of one request staged in LDS
+constexpr int kAlphaThreads = 256;
+constexpr int kNone = 0x7FFFFFFF;
+static_assert(kChunkBlocks == kFinWaves, "a bonus chunk is rescanned one block per wave");
+static_assert(sdv::kMaxChunks <= kFinThreads, "chunk locate assumes one chunk per thread");
 
 struct VerifyArgs {
   const char* tgt;
@@ -65,57 +61,21 @@ struct VerifyArgs {
   int32_t* status;
   float* probe_probs;
   float* row_stats;
-  float* accept_prob;  // [R][gmax] or null
-  float2* partial;  // [R][S][n_ch][kWaves]
-  float* row_ref;   // [R][S] fp32(max * c) of every batch row
-  double* row_z;    // [R][S] sum 2^(x*c - ref)
-  double* asum;     // [R][gmax][n_ch][kWaves] chunk sums of min(p, q)
-  Plan* plans;      // [R]
-  double* rsum;     // [R][n_ch][kWaves]
+  float* accept_prob;     // [R][gmax] or null
+  const float2* partial;  // [R][S][n_ch][kRowWaves] from the bandwidth pass
+  float* row_ref;         // [R][S] fp32(max * c) of every batch row
+  double* row_z;          // [R][S] sum 2^(x*c - ref)
+  double* bsum;           // [R][n_blk] residual mass per 1024-element block
+  double* asum;           // [R][gmax][n_ch][kRowWaves] chunk sums of min(p, q)
   int64_t ld_bytes;
   uint64_t seed;
-  float c;          // log2(e) / T
+  float c;                // log2(e) / T
   float inv_t;
   int gmax;
   int V;
   int n_ch;
+  int n_blk;
 };
-
-// 16-byte vector of logits -> floats.  bf16: 8 values, fp32: 4 values.
-template <bool BF16>
-struct Vec;
-template <>
-struct Vec<true> {
-  static constexpr int kElems = 8;
-  static constexpr int kBytes = 2;
-  static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
-  __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
-    x[0] = sdv::bf16lo(v.x); x[1] = sdv::bf16hi(v.x);
-    x[2] = sdv::bf16lo(v.y); x[3] = sdv::bf16hi(v.y);
-    x[4] = sdv::bf16lo(v.z); x[5] = sdv::bf16hi(v.z);
-    x[6] = sdv::bf16lo(v.w); x[7] = sdv::bf16hi(v.w);
-  }
-  __device__ __forceinline__ static float at(const char* row, int v) {
-    return sdv::bf16_to_f32(((const uint16_t*)row)[v]);
-  }
-};
-template <>
-struct Vec<false> {
-  static constexpr int kElems = 4;
-  static constexpr int kBytes = 4;
-  static constexpr uint32_t kNegInfWord = 0xFF800000u;
-  __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
-    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
-  }
-  __device__ __forceinline__ static float at(const char* row, int v) {
-    return ((const float*)row)[v];
-  }
-};
-
-// Reference exponent for a max m: fp32(m * c); 0 when nothing finite was seen
-// (then every contribution is 2^-inf = 0, or NaN if a NaN was present).
-__device__ __forceinline__ float exp_ref(float m, float c) { return m == kNegInf ? 0.0f : m * c; }
 
 __device__ __forceinline__ int row_status(float M, double Z) {
   if (isnan(M) || isnan(Z) || M == __builtin_huge_valf()) return SD_ST_NONFINITE;
@@ -123,79 +83,112 @@ __device__ __forceinline__ int row_status(float M, double Z) {
   return 0;
 }
 
-__device__ __forceinline__ bool slot_in_batch(int slot, int gmax, int L) {
-  return slot <= gmax ? slot <= L : slot - gmax <= L;
+// Weight of one element of the correction draw: residual max(0, p - q)
+// (kind 1) or the unnormalised target law 2^(x*c - ref) (kind 2); fp64 from
+// fp32 exponentials.
+__device__ __forceinline__ double draw_weight(float xt, float xd, int kind, float c, float mct,
+                                              double izt, float mcd, double izd) {
+  const double et = (double)sdv::fast_exp2(fmaf(xt, c, -mct));
+  if (kind != 1) return et;
+  const double ed = (double)sdv::fast_exp2(fmaf(xd, c, -mcd));
+  return fmax(0.0, et * izt - ed * izd);
+}
+
+struct DrawParams {
+  int kind;
+  float c, mct, mcd;
+  double izt, izd;
+};
+
+// One wave scans one 1024-element block held in registers (lane l holds
+// vectors k*64 + l of the block, vocabulary order (k, lane, element)) for the
+// first element whose running sum of weights exceeds `rem`.  Returns that
+// element's row index, or kNone; *last gets the block's last index with
+// positive weight (or -1).  Wave-uniform results.
+template <bool BF16, int VL>
+__device__ int wave_block_scan(const uint4 (&tv)[VL], const uint4 (&dv)[VL], int vbase,
+                               const DrawParams& dp, double rem, int lane, int* last) {
+  using VT = sdv::Vec<BF16>;
+  double col[VL];
+  int lst = -1;
+#pragma unroll
+  for (int k = 0; k < VL; ++k) {
+    float xt[VT::kElems], xd[VT::kElems];
+    VT::unpack(tv[k], xt);
+    VT::unpack(dv[k], xd);
+    double vs = 0.0;
+#pragma unroll
+    for (int e = 0; e < VT::kElems; ++e) {
+      const double w = draw_weight(xt[e], xd[e], dp.kind, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
+      vs += w;
+      if (w > 0.0) lst = (vbase + k * 64 + lane) * VT::kElems + e;
+    }
+    col[k] = vs;
+  }
+  *last = -sdv::wave_min_i(-lst);
+  double run = 0.0;
+#pragma unroll
+  for (int k = 0; k < VL; ++k) {  // unrolled: the arrays stay in registers
+    const double incl = sdv::wave_incl_scan_d(col[k], lane);
+    const double c0 = run + (incl - col[k]);
+    int hit = kNone;
+    if (c0 <= rem && c0 + col[k] > rem) {
+      float xt[VT::kElems], xd[VT::kElems];
+      VT::unpack(tv[k], xt);
+      VT::unpack(dv[k], xd);
+      double cc = c0;
+      for (int e = 0; e < VT::kElems; ++e) {
+        cc += draw_weight(xt[e], xd[e], dp.kind, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
+        if (cc > rem) {
+          hit = (vbase + k * 64 + lane) * VT::kElems + e;
+          break;
+        }
+      }
+    }
+    hit = sdv::wave_min_i(hit);
+    if (hit != kNone) return hit;
+    run += __shfl(incl, 63, 64);
+  }
+  return kNone;
+}
+
+// Inclusive prefix sum over the workgroup in thread order (every thread calls).
+__device__ __forceinline__ double block_incl_scan(double v, int lane, int wave, double* s_w) {
+  const double incl = sdv::wave_incl_scan_d(v, lane);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  double off = 0.0;
+  for (int w = 0; w < wave; ++w) off += s_w[w];
+  __syncthreads();
+  return off + incl;
 }
 
 // ---------------------------------------------------------------------------
-// The bandwidth pass.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_row_partials(VerifyArgs a) {
-  using VT = Vec<BF16>;
-  constexpr int kVec = kChunk / VT::kElems / kThreads;
-  const int item = blockIdx.x;
-  const int S = 2 * a.gmax + 1;
-  const int ch = item % a.n_ch;
-  const int rs = item / a.n_ch;
-  const int slot = rs % S, r = rs / S;
-  const int L = sdv::clampi(a.ell[r], 0, a.gmax);
-  if (!slot_in_batch(slot, a.gmax, L)) return;
-  const char* row = slot <= a.gmax
-                        ? a.tgt + ((int64_t)a.tgt_row0[r] + slot) * a.ld_bytes
-                        : a.drf + ((int64_t)a.drf_row0[r] + (slot - a.gmax - 1)) * a.ld_bytes;
-  const int e0 = ch * kChunk;
-  const int nvec = min(kChunk, a.V - e0) / VT::kElems;
-  const uint4* p = (const uint4*)(row + (int64_t)e0 * VT::kBytes);
-  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
-  const float c = a.c;
-
-  uint4 buf[kVec];
-#pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    const int v = threadIdx.x + k * kThreads;
-    buf[k] = v < nvec ? sdv::ld_nt(p + v) : ninf;
-  }
-  float m = kNegInf;
-#pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    float x[VT::kElems];
-    VT::unpack(buf[k], x);
-#pragma unroll
-    for (int e = 0; e < VT::kElems; ++e) m = fmaxf(m, x[e]);
-  }
-  const float ref = exp_ref(m, c);
-  float s = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    float x[VT::kElems];
-    VT::unpack(buf[k], x);
-#pragma unroll
-    for (int e = 0; e < VT::kElems; ++e) s += sdv::fast_exp2(fmaf(x[e], c, -ref));
-  }
-  // wave partial: rescale every lane to the wave max
-  const float wm = sdv::wave_max(m);
-  const float wref = exp_ref(wm, c);
-  const float ws = sdv::wave_sum((s == 0.0f) ? 0.0f : s * sdv::fast_exp2(ref - wref));
-  if ((threadIdx.x & 63) == 0)
-    a.partial[((size_t)rs * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = make_float2(wm, ws);
-}
-
-// ---------------------------------------------------------------------------
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
-  using VT = Vec<BF16>;
+__global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
+  using VT = sdv::Vec<BF16>;
+  constexpr int VL = kBlk / VT::kElems / 64;  // vectors per lane per row of a block
+  constexpr int kBlkVec = kBlk / VT::kElems;
   __shared__ float sM[kMaxSlots];
   __shared__ float sRef[kMaxSlots];
   __shared__ double sZ[kMaxSlots];
   __shared__ float2 sPart[kStagedParts];
-  __shared__ int s_st, s_jstar, s_zero_q_upto;
+  __shared__ double s_incl[kFinThreads];
+  __shared__ double s_w[kFinWaves];
+  __shared__ int s_st, s_jstar, s_zero_q_upto, s_owner, s_blk, s_tok, s_last;
+  __shared__ double s_rem;
 
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gmax = a.gmax, S = 2 * gmax + 1, V = a.V;
   const int L = sdv::clampi(a.ell[r], 0, gmax);
-  const int nparts = a.n_ch * kWaves;
+  const int nparts = a.n_ch * kRowWaves;
   const float c = a.c;
-  if (tid == 0) { s_st = 0; s_jstar = L + 1; s_zero_q_upto = 0x7FFFFFFF; }
+  if (tid == 0) {
+    s_st = 0;
+    s_jstar = L + 1;
+    s_zero_q_upto = kNone;
+    s_owner = kNone;
+  }
 
   // Stage the partials of the batch rows (target slots 0..L, then draft slots
   // gmax+1..gmax+L, i.e. local row b) in LDS when they fit: one load each.
@@ -203,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   const bool staged = (long long)nrows * nparts <= kStagedParts;
   const float2* base = a.partial + (size_t)r * S * nparts;
   if (staged) {
-    for (int i = tid; i < nrows * nparts; i += kThreads) {
+    for (int i = tid; i < nrows * nparts; i += kFinThreads) {
       const int b = i / nparts, q = i % nparts;
       const int slot = b <= L ? b : gmax + (b - L);
       sPart[i] = base[(size_t)slot * nparts + q];
@@ -211,20 +204,20 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   }
   __syncthreads();
 
-  // (m, Z) per row: 16 groups of 16 lanes, one row per group at a time
+  // (m, Z) per row: groups of 16 lanes, one row per group at a time
   const int grp = tid >> 4, gl = tid & 15;
-  for (int b = grp; b < nrows; b += kThreads / 16) {
+  for (int b = grp; b < nrows; b += kFinThreads / 16) {
     const int slot = b <= L ? b : gmax + (b - L);
     const float2* pp = staged ? sPart + b * nparts : base + (size_t)slot * nparts;
     float M = kNegInf;
     for (int q = gl; q < nparts; q += 16) M = fmaxf(M, pp[q].x);
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
-    const float ref = exp_ref(M, c);
+    const float ref = sdv::exp_ref(M, c);
     double Z = 0.0;
     for (int q = gl; q < nparts; q += 16) {
       const float2 v = pp[q];
-      if (v.y != 0.0f) Z += (double)v.y * (double)sdv::fast_exp2(exp_ref(v.x, c) - ref);
+      if (v.y != 0.0f) Z += (double)v.y * (double)sdv::fast_exp2(sdv::exp_ref(v.x, c) - ref);
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) Z += __shfl_xor(Z, o, 16);
@@ -247,14 +240,12 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   }
   __syncthreads();
 
-  Plan* plan = a.plans + r;
   int32_t* out_tok = a.out_tokens + (size_t)r * (gmax + 1);
   if (s_st) {  // a needed row is unusable: the request fails
-    for (int t = tid; t <= gmax; t += kThreads) out_tok[t] = -1;
+    for (int t = tid; t <= gmax; t += kFinThreads) out_tok[t] = -1;
     if (tid == 0) {
       a.n_accepted[r] = 0;
       a.status[r] = s_st;
-      plan->kind = 0;
     }
     return;
   }
@@ -262,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   // every accept test at once; the chain stops at the first rejection
   const int64_t pbase = a.pos0 ? a.pos0[r] : 0;
   const int32_t* drafts = a.draft_tokens + (size_t)r * gmax;
-  for (int j = tid + 1; j <= L; j += kThreads) {
+  for (int j = tid + 1; j <= L; j += kFinThreads) {
     const int x = drafts[j - 1];
     bool reject;
     if (x < 0 || x >= V) {
@@ -292,103 +283,239 @@ __global__ __launch_bounds__(kThreads) void k_accept(VerifyArgs a) {
   const int jstar = s_jstar;
   const bool rejected = jstar <= L;
   const int n = rejected ? jstar - 1 : L;
-  for (int t = tid; t <= gmax; t += kThreads) out_tok[t] = (t < n) ? drafts[t] : -1;
-  if (tid == 0) {
-    int st = 0;
-    if (s_zero_q_upto <= (rejected ? jstar : L)) st |= SD_ST_ZERO_Q;
-    if (rejected) {
-      const int x = drafts[jstar - 1];
-      if (x < 0 || x >= V) st |= SD_ST_BAD_TOKEN;
+  for (int t = tid; t <= gmax; t += kFinThreads) out_tok[t] = (t < n) ? drafts[t] : -1;
+  int st = 0;
+  if (s_zero_q_upto <= (rejected ? jstar : L)) st |= SD_ST_ZERO_Q;
+  if (rejected) {
+    const int x = drafts[jstar - 1];
+    if (x < 0 || x >= V) st |= SD_ST_BAD_TOKEN;
+  }
+
+  // The correction draw.
+  const int pos = rejected ? jstar : L + 1;
+  const double u = sdv::uniform24(a.seed, (uint64_t)r, (uint64_t)(pbase + pos), 2);
+  const int tslot = pos - 1;
+  const char* trow = a.tgt + ((int64_t)a.tgt_row0[r] + (pos - 1)) * a.ld_bytes;
+  const char* drow = rejected ? a.drf + ((int64_t)a.drf_row0[r] + (jstar - 1)) * a.ld_bytes : trow;
+  DrawParams dp;
+  dp.kind = rejected ? 1 : 2;
+  dp.c = c;
+  dp.mct = sRef[tslot];
+  dp.izt = 1.0 / sZ[tslot];
+  dp.mcd = rejected ? sRef[gmax + jstar] : 0.0f;
+  dp.izd = rejected ? 1.0 / sZ[gmax + jstar] : 1.0;
+  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  const int nvec = V / VT::kElems;
+  const uint4* tp = (const uint4*)trow;
+  const uint4* dq = (const uint4*)drow;
+  double* bsum = a.bsum + (size_t)r * a.n_blk;
+  const int n_blk = a.n_blk;
+
+  double target = 0.0;
+  if (dp.kind == 1) {
+    // Residual mass per block: wave w streams blocks w, w + 16, ... with the
+    // next block's loads issued before the current block is summed.
+    uint4 ct[VL], cd[VL];
+    auto load = [&](int b, uint4 (&t)[VL], uint4 (&d)[VL]) {
+#pragma unroll
+      for (int k = 0; k < VL; ++k) {
+        const int v = b * kBlkVec + k * 64 + lane;
+        t[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
+        d[k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
+      }
+    };
+    if (wave < n_blk) load(wave, ct, cd);
+    for (int b = wave; b < n_blk; b += kFinWaves) {
+      uint4 nt[VL], nd[VL];
+      if (b + kFinWaves < n_blk) {
+        load(b + kFinWaves, nt, nd);
+      } else {
+#pragma unroll
+        for (int k = 0; k < VL; ++k) nt[k] = nd[k] = ninf;
+      }
+      double acc = 0.0;
+#pragma unroll
+      for (int k = 0; k < VL; ++k) {
+        float xt[VT::kElems], xd[VT::kElems];
+        VT::unpack(ct[k], xt);
+        VT::unpack(cd[k], xd);
+#pragma unroll
+        for (int e = 0; e < VT::kElems; ++e)
+          acc += draw_weight(xt[e], xd[e], 1, c, dp.mct, dp.izt, dp.mcd, dp.izd);
+      }
+      acc = sdv::wave_sum_d(acc);
+      if (lane == 0) bsum[b] = acc;
+#pragma unroll
+      for (int k = 0; k < VL; ++k) {
+        ct[k] = nt[k];
+        cd[k] = nd[k];
+      }
     }
+    __syncthreads();  // block sums of every wave visible to the workgroup
+
+    // thread t owns the contiguous run of blocks [t*per, (t+1)*per)
+    const int per = (n_blk + kFinThreads - 1) / kFinThreads;
+    const int b0 = min(tid * per, n_blk), b1 = min(b0 + per, n_blk);
+    double tot = 0.0;
+    for (int b = b0; b < b1; ++b) tot += bsum[b];
+    const double incl = block_incl_scan(tot, lane, wave, s_w);
+    s_incl[tid] = incl;
+    __syncthreads();
+    const double total = s_incl[kFinThreads - 1];
+    if (total > 0.0) {
+      target = u * total;
+      if (incl > target) atomicMin(&s_owner, tid);
+      __syncthreads();
+      if (tid == s_owner) {  // walk the run: first block whose running sum passes
+        double acc = tid == 0 ? 0.0 : s_incl[tid - 1];
+        int blk = -1, lastpos = -1;
+        double rem = __builtin_huge_val();
+        for (int b = b0; b < b1; ++b) {
+          const double w = bsum[b];
+          if (w > 0.0) lastpos = b;
+          if (acc + w > target) {
+            blk = b;
+            rem = target - acc;
+            break;
+          }
+          acc += w;
+        }
+        if (blk < 0) blk = lastpos;  // rounding: last block with mass, its last element
+        s_blk = blk;
+        s_rem = rem;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int blk = s_blk;
+        if (blk < 0) {  // no block with mass (not reachable when total > 0)
+          if (lane == 0) {
+            out_tok[n] = -1;
+            a.n_accepted[r] = n;
+            a.status[r] = st;
+          }
+          return;
+        }
+        uint4 tv[VL], dv[VL];
+#pragma unroll
+        for (int k = 0; k < VL; ++k) {
+          const int v = blk * kBlkVec + k * 64 + lane;
+          tv[k] = v < nvec ? tp[v] : ninf;
+          dv[k] = v < nvec ? dq[v] : ninf;
+        }
+        int last;
+        int tok = wave_block_scan<BF16, VL>(tv, dv, blk * kBlkVec, dp, s_rem, lane, &last);
+        if (tok == kNone) tok = last;
+        if (lane == 0) {
+          out_tok[n] = tok;
+          a.n_accepted[r] = n;
+          a.status[r] = st;
+        }
+      }
+      return;
+    }
+    // empty residual: draw from p_j* instead
+    st |= SD_ST_ZERO_RESIDUAL;
+    dp.kind = 2;
+    dp.mcd = 0.0f;
+    dp.izd = 1.0;
+    drow = trow;
+    dq = tp;
+  }
+
+  // Draw from the target law of slot tslot: chunk sums from the first pass
+  // (thread t = chunk t), the crossing chunk by a workgroup prefix sum, then
+  // each wave sums one 1024-element block of that chunk and the wave holding
+  // the crossing scans its block.
+  const int n_ch = a.n_ch;
+  double tot = 0.0;
+  if (tid < n_ch) {
+    const float2* pp = a.partial + ((size_t)r * S + tslot) * nparts + (size_t)tid * kRowWaves;
+    for (int w = 0; w < kRowWaves; ++w) {
+      const float2 q = pp[w];
+      if (q.y != 0.0f) tot += (double)q.y * exp2((double)sdv::exp_ref(q.x, c) - (double)dp.mct);
+    }
+  }
+  const double incl = block_incl_scan(tot, lane, wave, s_w);
+  s_incl[tid] = incl;
+  __syncthreads();
+  target = u * s_incl[kFinThreads - 1];
+  if (incl > target && tid < n_ch) atomicMin(&s_owner, tid);
+  if (tid == 0) {
+    s_last = -1;
+    s_tok = kNone;
+  }
+  __syncthreads();
+  int ch = s_owner;
+  double rem;
+  if (ch == kNone) {  // rounding put the target past the end: last chunk with mass
+    int lp = -1;
+    for (int t = 0; t < n_ch; ++t)
+      if (s_incl[t] > (t == 0 ? 0.0 : s_incl[t - 1])) lp = t;
+    ch = lp;
+    rem = __builtin_huge_val();
+  } else {
+    rem = target - (ch == 0 ? 0.0 : s_incl[ch - 1]);
+  }
+  if (ch < 0) {  // no mass anywhere (not reachable for a finite row)
+    if (tid == 0) {
+      out_tok[n] = -1;
+      a.n_accepted[r] = n;
+      a.status[r] = st;
+    }
+    return;
+  }
+  const int blk = ch * kChunkBlocks + wave;
+  uint4 tv[VL], dv[VL];
+#pragma unroll
+  for (int k = 0; k < VL; ++k) {
+    const int v = blk * kBlkVec + k * 64 + lane;
+    tv[k] = v < nvec ? tp[v] : ninf;
+    dv[k] = ninf;
+  }
+  double wsum = 0.0;
+#pragma unroll
+  for (int k = 0; k < VL; ++k) {
+    float xt[VT::kElems];
+    VT::unpack(tv[k], xt);
+#pragma unroll
+    for (int e = 0; e < VT::kElems; ++e) wsum += (double)sdv::fast_exp2(fmaf(xt[e], c, -dp.mct));
+  }
+  wsum = sdv::wave_sum_d(wsum);
+  if (lane == 0) s_w[wave] = wsum;
+  __syncthreads();
+  double before = 0.0;
+  for (int w = 0; w < wave; ++w) before += s_w[w];
+  // the waves' intervals [before, before + wsum) partition the chunk's mass
+  const bool mine = before <= rem && before + wsum > rem;
+  int last;
+  // every wave scans (for its last positive element); only the owner's hit counts
+  const int tok = wave_block_scan<BF16, VL>(tv, dv, blk * kBlkVec, dp, mine ? rem - before : -1.0,
+                                            lane, &last);
+  if (lane == 0) {
+    if (mine && tok != kNone) s_tok = tok;
+    if (last >= 0) atomicMax(&s_last, last);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    out_tok[n] = s_tok != kNone ? s_tok : s_last;  // rounding: last element with mass
     a.n_accepted[r] = n;
     a.status[r] = st;
-    Plan pl;
-    pl.n_acc = n;
-    pl.st = st;
-    const int pos = rejected ? jstar : L + 1;
-    pl.u = sdv::uniform24(a.seed, (uint64_t)r, (uint64_t)(pbase + pos), 2);
-    pl.tslot = pos - 1;
-    pl.trow = (int64_t)a.tgt_row0[r] + (pos - 1);
-    pl.mct = sRef[pos - 1];
-    pl.zt = sZ[pos - 1];
-    if (rejected) {
-      pl.kind = 1;
-      pl.drow = (int64_t)a.drf_row0[r] + (jstar - 1);
-      pl.mcd = sRef[gmax + jstar];
-      pl.zd = sZ[gmax + jstar];
-    } else {
-      pl.kind = 2;
-      pl.drow = -1;
-      pl.mcd = 0.0f;
-      pl.zd = 1.0;
-    }
-    *plan = pl;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Weight of element e of the correction draw: residual max(0, p - q)
-// (kind 1) or the unnormalised target law 2^(x*c - ref) (kind 2); fp64 from
-// fp32 exponentials.
-__device__ __forceinline__ double draw_weight(float xt, float xd, int kind, float c, float mct,
-                                              double izt, float mcd, double izd) {
-  const double et = (double)sdv::fast_exp2(fmaf(xt, c, -mct));
-  if (kind != 1) return et;
-  const double ed = (double)sdv::fast_exp2(fmaf(xd, c, -mcd));
-  return fmax(0.0, et * izt - ed * izd);
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_residual_sums(VerifyArgs a) {
-  using VT = Vec<BF16>;
-  constexpr int kVec = kChunk / VT::kElems / kThreads;
-  const int r = blockIdx.x / a.n_ch, ch = blockIdx.x % a.n_ch;
-  const Plan pl = a.plans[r];
-  if (pl.kind != 1) return;
-  const int e0 = ch * kChunk;
-  const int nvec = min(kChunk, a.V - e0) / VT::kElems;
-  const uint4* tp = (const uint4*)(a.tgt + pl.trow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
-  const uint4* dp = (const uint4*)(a.drf + pl.drow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
-  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
-  const double izt = 1.0 / pl.zt, izd = 1.0 / pl.zd;
-  double acc = 0.0;
-  // two halves of the thread's vectors keep the kernel within 64 VGPRs
-  constexpr int kHalf = kVec / 2;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint4 tv[kHalf], dv[kHalf];
-#pragma unroll
-    for (int k = 0; k < kHalf; ++k) {
-      const int v = threadIdx.x + (h * kHalf + k) * kThreads;
-      tv[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
-      dv[k] = v < nvec ? sdv::ld_nt(dp + v) : ninf;
-    }
-#pragma unroll
-    for (int k = 0; k < kHalf; ++k) {
-      float xt[VT::kElems], xd[VT::kElems];
-      VT::unpack(tv[k], xt);
-      VT::unpack(dv[k], xd);
-#pragma unroll
-      for (int e = 0; e < VT::kElems; ++e)
-        acc += draw_weight(xt[e], xd[e], 1, a.c, pl.mct, izt, pl.mcd, izd);
-    }
-  }
-  acc = sdv::wave_sum_d(acc);
-  if ((threadIdx.x & 63) == 0) a.rsum[((size_t)r * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = acc;
 }
 
 // ---------------------------------------------------------------------------
 // Acceptance rate of position j: sum over the vocabulary of min(p_j, q_j).
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_alpha_sums(VerifyArgs a) {
-  using VT = Vec<BF16>;
+__global__ __launch_bounds__(sdv::kRowThreads) void k_alpha_sums(VerifyArgs a) {
+  using VT = sdv::Vec<BF16>;
+  constexpr int kThreads = sdv::kRowThreads;
   constexpr int kVec = kChunk / VT::kElems / kThreads;
   const int gmax = a.gmax, S = 2 * gmax + 1;
   const int ch = blockIdx.x % a.n_ch;
   const int rj = blockIdx.x / a.n_ch;
   const int j = rj % gmax + 1, r = rj / gmax;
   const int L = sdv::clampi(a.ell[r], 0, gmax);
-  if (j > L || a.plans[r].kind == 0) return;
+  if (j > L || (a.status[r] & (SD_ST_NONFINITE | SD_ST_ZERO_Z))) return;
   const float mct = a.row_ref[(size_t)r * S + (j - 1)];
   const float mcd = a.row_ref[(size_t)r * S + gmax + j];
   const double izt = 1.0 / a.row_z[(size_t)r * S + (j - 1)];
@@ -424,206 +551,48 @@ __global__ __launch_bounds__(kThreads) void k_alpha_sums(VerifyArgs a) {
   }
   acc = sdv::wave_sum_d(acc);
   if ((threadIdx.x & 63) == 0)
-    a.asum[(((size_t)r * gmax + (j - 1)) * a.n_ch + ch) * kWaves + (threadIdx.x >> 6)] = acc;
+    a.asum[(((size_t)r * gmax + (j - 1)) * a.n_ch + ch) * kRowWaves + (threadIdx.x >> 6)] = acc;
 }
 
-// ---------------------------------------------------------------------------
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_sample(VerifyArgs a) {
-  using VT = Vec<BF16>;
-  constexpr int kQuarterVec = kChunk / VT::kElems / kWaves;  // vectors per wave
-  constexpr int kPerLane = kQuarterVec / 64;                  // vectors per lane
-  __shared__ double s_chunk[kMaxChunks];
-  __shared__ double s_wave_tot[kWaves];
-  __shared__ int s_ch, s_found, s_last, s_kind;
-  __shared__ double s_target;
-
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const Plan pl = a.plans[r];
-  if (pl.kind == 0) return;
-  const int S = 2 * a.gmax + 1, n_ch = a.n_ch, V = a.V;
-  if (a.accept_prob) {  // per-row totals of the min(p, q) chunk sums
-    const int L = sdv::clampi(a.ell[r], 0, a.gmax);
-    for (int j = tid + 1; j <= a.gmax; j += kThreads) {
-      double t = 0.0;
-      if (j <= L) {
-        const double* q = a.asum + ((size_t)r * a.gmax + (j - 1)) * n_ch * kWaves;
-        for (int i = 0; i < n_ch * kWaves; ++i) t += q[i];
-      }
-      a.accept_prob[(size_t)r * a.gmax + (j - 1)] = (float)t;
-    }
+// Per-row totals of the min(p, q) chunk sums; 0 past l_r and for a failed
+// request.
+__global__ __launch_bounds__(kAlphaThreads) void k_alpha_total(VerifyArgs a, int R) {
+  const int i = blockIdx.x * kAlphaThreads + threadIdx.x;
+  if (i >= R * a.gmax) return;
+  const int r = i / a.gmax, j = i % a.gmax + 1;
+  const int L = sdv::clampi(a.ell[r], 0, a.gmax);
+  double t = 0.0;
+  if (j <= L && !(a.status[r] & (SD_ST_NONFINITE | SD_ST_ZERO_Z))) {
+    const double* q = a.asum + ((size_t)r * a.gmax + (j - 1)) * a.n_ch * kRowWaves;
+    for (int k = 0; k < a.n_ch * kRowWaves; ++k) t += q[k];
   }
-  const float c = a.c;
-  int st = pl.st;
-
-  // chunk sums of the weights
-  if (pl.kind == 1) {
-    for (int ch = tid; ch < n_ch; ch += kThreads) {
-      const double* q = a.rsum + ((size_t)r * n_ch + ch) * kWaves;
-      s_chunk[ch] = (q[0] + q[1]) + (q[2] + q[3]);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double tot = 0.0;
-      for (int ch = 0; ch < n_ch; ++ch) tot += s_chunk[ch];
-      s_kind = (tot > 0.0) ? 1 : 2;  // empty residual: draw from p_j* instead
-    }
-  } else if (tid == 0) {
-    s_kind = 2;
-  }
-  __syncthreads();
-  const int kind = s_kind;
-  if (pl.kind == 1 && kind == 2) st |= SD_ST_ZERO_RESIDUAL;
-  if (kind == 2) {  // sum over chunk ch of 2^(x*c - mct), from the first pass
-    const float2* pp = a.partial + ((size_t)r * S + pl.tslot) * n_ch * kWaves;
-    for (int ch = tid; ch < n_ch; ch += kThreads) {
-      double sum = 0.0;
-      for (int w = 0; w < kWaves; ++w) {
-        const float2 q = pp[ch * kWaves + w];
-        if (q.y != 0.0f) sum += (double)q.y * exp2((double)exp_ref(q.x, c) - (double)pl.mct);
-      }
-      s_chunk[ch] = sum;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    double tot = 0.0;
-    for (int ch = 0; ch < n_ch; ++ch) tot += s_chunk[ch];
-    const double target = pl.u * tot;
-    double acc = 0.0;
-    int found = -1, last_pos = -1;
-    for (int ch = 0; ch < n_ch; ++ch) {
-      if (s_chunk[ch] > 0.0) last_pos = ch;
-      if (found < 0 && acc + s_chunk[ch] > target) found = ch;
-      if (found < 0) acc += s_chunk[ch];
-    }
-    if (found < 0) {  // rounding put the target past the end: take the last mass
-      found = last_pos;
-      s_target = __builtin_huge_val();
-    } else {
-      s_target = target - acc;
-    }
-    s_ch = found;
-    s_found = 0x7FFFFFFF;
-    s_last = -1;
-  }
-  __syncthreads();
-  const int ch = s_ch;
-  int32_t* out_tok = a.out_tokens + (size_t)r * (a.gmax + 1);
-  if (ch < 0) {  // no mass anywhere (not reachable for a finite row)
-    if (tid == 0) {
-      out_tok[pl.n_acc] = -1;
-      a.status[r] = st;
-    }
-    return;
-  }
-
-  // Rescan the chunk: wave w owns the contiguous quarter
-  // [w*kQuarterVec, (w+1)*kQuarterVec) of its vectors, lane l the vectors
-  // w*kQuarterVec + k*64 + l; vocabulary order is (k, lane, element).
-  const double target = s_target;
-  const int e0 = ch * kChunk;
-  const int nvec = min(kChunk, V - e0) / VT::kElems;
-  const uint4* tp = (const uint4*)(a.tgt + pl.trow * a.ld_bytes + (int64_t)e0 * VT::kBytes);
-  const uint4* dp = kind == 1 ? (const uint4*)(a.drf + pl.drow * a.ld_bytes + (int64_t)e0 * VT::kBytes)
-                              : nullptr;
-  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
-  const double izt = 1.0 / pl.zt, izd = 1.0 / pl.zd;
-  uint4 tv[kPerLane], dv[kPerLane];
-#pragma unroll
-  for (int k = 0; k < kPerLane; ++k) {
-    const int v = wave * kQuarterVec + k * 64 + lane;
-    tv[k] = v < nvec ? tp[v] : ninf;
-    dv[k] = (v < nvec && dp) ? dp[v] : ninf;
-  }
-  double col[kPerLane];
-  double my_tot = 0.0;
-  int last = -1;
-#pragma unroll
-  for (int k = 0; k < kPerLane; ++k) {
-    float xt[VT::kElems], xd[VT::kElems];
-    VT::unpack(tv[k], xt);
-    VT::unpack(dv[k], xd);
-    double vs = 0.0;
-#pragma unroll
-    for (int e = 0; e < VT::kElems; ++e) {
-      const double w = draw_weight(xt[e], xd[e], kind, c, pl.mct, izt, pl.mcd, izd);
-      vs += w;
-      if (w > 0.0) last = e0 + (wave * kQuarterVec + k * 64 + lane) * VT::kElems + e;
-    }
-    col[k] = vs;
-    my_tot += vs;
-  }
-  const double wtot = sdv::wave_sum_d(my_tot);
-  if (lane == 0) s_wave_tot[wave] = wtot;
-  if (last >= 0) atomicMax(&s_last, last);
-  __syncthreads();
-  double run = 0.0;
-  for (int w = 0; w < wave; ++w) run += s_wave_tot[w];
-  if (run <= target && run + s_wave_tot[wave] > target) {
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) {
-      const double incl = sdv::wave_incl_scan_d(col[k], lane);
-      const double c0 = run + (incl - col[k]);
-      int hit = 0x7FFFFFFF;
-      if (c0 <= target && c0 + col[k] > target) {
-        float xt[VT::kElems], xd[VT::kElems];
-        VT::unpack(tv[k], xt);
-        VT::unpack(dv[k], xd);
-        double cc = c0;
-        for (int e = 0; e < VT::kElems; ++e) {
-          cc += draw_weight(xt[e], xd[e], kind, c, pl.mct, izt, pl.mcd, izd);
-          if (cc > target) {
-            hit = e0 + (wave * kQuarterVec + k * 64 + lane) * VT::kElems + e;
-            break;
-          }
-        }
-      }
-      hit = sdv::wave_min_i(hit);
-      if (hit != 0x7FFFFFFF) {
-        if (lane == 0) atomicMin(&s_found, hit);
-        break;
-      }
-      run += __shfl(incl, 63, 64);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int token = s_found;
-    if (token == 0x7FFFFFFF) token = s_last;  // rounding: last element with mass
-    out_tok[pl.n_acc] = token;
-    a.status[r] = st;
-  }
+  a.accept_prob[i] = (float)t;
 }
 
 size_t partial_bytes(int R, int gmax, int V) {
   const size_t n_ch = ((size_t)V + kChunk - 1) / kChunk;
-  return sdv_align256((size_t)R * (2 * (size_t)gmax + 1) * n_ch * kWaves * sizeof(float2));
+  return sdv_align256((size_t)R * (2 * (size_t)gmax + 1) * n_ch * kRowWaves * sizeof(float2));
 }
 
 size_t verify_ws_bytes(int R, int gmax, int V) {
   const size_t n_ch = ((size_t)V + kChunk - 1) / kChunk;
+  const size_t n_blk = ((size_t)V + kBlk - 1) / kBlk;
   const size_t S = 2 * (size_t)gmax + 1;
-  return partial_bytes(R, gmax, V) + sdv_align256((size_t)R * sizeof(Plan)) +
-         sdv_align256((size_t)R * n_ch * kWaves * sizeof(double)) +
-         sdv_align256((size_t)R * S * sizeof(float)) + sdv_align256((size_t)R * S * sizeof(double)) +
-         sdv_align256((size_t)R * gmax * n_ch * kWaves * sizeof(double));
+  return partial_bytes(R, gmax, V) + sdv_align256((size_t)R * S * sizeof(float)) +
+         sdv_align256((size_t)R * S * sizeof(double)) +
+         sdv_align256((size_t)R * n_blk * sizeof(double)) +
+         sdv_align256((size_t)R * gmax * n_ch * kRowWaves * sizeof(double));
 }
 
 template <bool BF16>
-int launch_verify(hipStream_t stream, int R, const VerifyArgs& a, long long items,
-                  hipEvent_t ev0, hipEvent_t ev1) {
-  const bool timed = ev0 && ev1;
-  if (timed) SDV_TRY_LAUNCH(hipEventRecord(ev0, stream));
-  SDV_TRY_LAUNCH(sdv::launch(k_row_partials<BF16>, dim3((unsigned)items), dim3(kThreads), 0, stream, a));
-  if (timed) SDV_TRY_LAUNCH(hipEventRecord(ev1, stream));
-  SDV_TRY_LAUNCH(sdv::launch(k_accept<BF16>, dim3(R), dim3(kThreads), 0, stream, a));
-  SDV_TRY_LAUNCH(sdv::launch(k_residual_sums<BF16>, dim3((unsigned)(R * a.n_ch)), dim3(kThreads), 0,
-                             stream, a));
-  if (a.accept_prob && a.gmax > 0)
+int launch_finish(hipStream_t stream, int R, const VerifyArgs& a) {
+  SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16>, dim3(R), dim3(kFinThreads), 0, stream, a));
+  if (a.accept_prob && a.gmax > 0) {
     SDV_TRY_LAUNCH(sdv::launch(k_alpha_sums<BF16>, dim3((unsigned)((long long)R * a.gmax * a.n_ch)),
-                               dim3(kThreads), 0, stream, a));
-  SDV_TRY_LAUNCH(sdv::launch(k_sample<BF16>, dim3(R), dim3(kThreads), 0, stream, a));
+                               dim3(sdv::kRowThreads), 0, stream, a));
+    const unsigned g = (unsigned)(((long long)R * a.gmax + kAlphaThreads - 1) / kAlphaThreads);
+    SDV_TRY_LAUNCH(sdv::launch(k_alpha_total, dim3(g), dim3(kAlphaThreads), 0, stream, a, R));
+  }
   return SD_OK;
 }
 
@@ -646,6 +615,7 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   if (gamma_max > SD_MAX_GAMMA || V > SD_MAX_VOCAB) return SD_EUNSUPPORTED;
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_EINVAL;
   if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf())) return SD_EINVAL;
+  if ((prof_start == nullptr) != (prof_stop == nullptr)) return SD_EINVAL;
   if (R == 0) return SD_OK;
   if (!tgt_logits || !tgt_row0 || !drf_row0 || !ell || !n_accepted || !out_tokens || !status)
     return SD_EINVAL;
@@ -657,11 +627,33 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   const int n_ch = (V + kChunk - 1) / kChunk;
   const long long items = (long long)R * (2 * gamma_max + 1) * n_ch;
   if (items > 0x7FFFFFFFLL) return SD_EUNSUPPORTED;
+  const int64_t ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
+  const float c = sdv::kLog2e / temperature;
+  const char* drf = (const char*)(drf_logits ? drf_logits : tgt_logits);
+  const size_t S = 2 * (size_t)gamma_max + 1;
+  const int n_blk = (V + kBlk - 1) / kBlk;
+
+  char* p = (char*)workspace;
+  float2* partial = (float2*)p;
+  p += partial_bytes(R, gamma_max, V);
+
+  sdv::RowPassArgs ra;
+  ra.tgt = (const char*)tgt_logits;
+  ra.tgt_row0 = tgt_row0;
+  ra.drf = drf;
+  ra.drf_row0 = drf_row0;
+  ra.ell = ell;
+  ra.partial = partial;
+  ra.ld_bytes = ld_bytes;
+  ra.c = c;
+  ra.gmax = gamma_max;
+  ra.V = V;
+  ra.n_ch = n_ch;
 
   VerifyArgs a;
   a.tgt = (const char*)tgt_logits;
   a.tgt_row0 = tgt_row0;
-  a.drf = (const char*)(drf_logits ? drf_logits : tgt_logits);
+  a.drf = drf;
   a.drf_row0 = drf_row0;
   a.draft_tokens = draft_tokens;
   a.ell = ell;
@@ -672,26 +664,26 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   a.probe_probs = probe_probs;
   a.row_stats = row_stats;
   a.accept_prob = accept_prob;
-  const size_t S = 2 * (size_t)gamma_max + 1;
-  char* p = (char*)workspace;
-  a.partial = (float2*)p;
-  p += partial_bytes(R, gamma_max, V);
-  a.plans = (Plan*)p;
-  p += sdv_align256((size_t)R * sizeof(Plan));
-  a.rsum = (double*)p;
-  p += sdv_align256((size_t)R * n_ch * kWaves * sizeof(double));
+  a.partial = partial;
   a.row_ref = (float*)p;
   p += sdv_align256((size_t)R * S * sizeof(float));
   a.row_z = (double*)p;
   p += sdv_align256((size_t)R * S * sizeof(double));
+  a.bsum = (double*)p;
+  p += sdv_align256((size_t)R * n_blk * sizeof(double));
   a.asum = (double*)p;
-  a.ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
+  a.ld_bytes = ld_bytes;
   a.seed = seed;
-  a.c = sdv::kLog2e / temperature;
+  a.c = c;
   a.inv_t = 1.0f / temperature;
   a.gmax = gamma_max;
   a.V = V;
   a.n_ch = n_ch;
-  if (dtype == SD_DTYPE_BF16) return launch_verify<true>(stream, R, a, items, prof_start, prof_stop);
-  return launch_verify<false>(stream, R, a, items, prof_start, prof_stop);
+  a.n_blk = n_blk;
+
+  const bool bf16 = dtype == SD_DTYPE_BF16;
+  if (prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
+  SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, (unsigned)items, stream));
+  if (prof_stop) SDV_TRY_LAUNCH(hipEventRecord(prof_stop, stream));
+  return bf16 ? launch_finish<true>(stream, R, a) : launch_finish<false>(stream, R, a);
 }

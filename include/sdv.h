@@ -173,8 +173,9 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *   accept_prob [R][gamma_max] fp32 or NULL: alpha_j = sum_v min(p_j(v), q_j(v)),
  *               the probability that position j is accepted given the prefix
  *               was, i.e. 1 - TV(p_j, q_j), the label the confidence head is
- *               trained on [DS 2.1]; 0 past ell.  Costs a second read of every
- *               verified row pair (not done when NULL).
+ *               trained on [DS 2.1]; 0 past ell and for a failed request.
+ *               Costs a second read of every verified row pair (not done
+ *               when NULL).
  * prof_start, prof_stop  optional HIP events (both or neither): recorded on
  *             `stream` right before and after the row-statistics pass (the
  *             bandwidth-bound kernel that streams every row once), so a caller
@@ -233,6 +234,21 @@ int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
                     const uint16_t* E, int rank_e, const float* w,
                     int32_t* tokens, uint16_t* q_logits, float* conf, int32_t* status,
                     void* workspace, size_t workspace_bytes);
+
+/*
+ * Measurement aid, not part of the method.
+ *
+ * sd_stream_read - stream `bytes` bytes of device memory at `src` with the
+ * load shape of sd_verify's bandwidth pass (256-thread workgroups, eight
+ * 16-byte non-temporal loads per thread, 32 KB per workgroup) and fold each
+ * workgroup's words into one uint32 of `sink`.  Timing it over a buffer of
+ * the verify batch's size gives the practical HBM read ceiling.
+ *   bytes >= 0, bytes % 16 == 0; src 16-byte aligned device memory;
+ *   sink: device memory for sd_stream_read_sink_words(bytes) uint32.
+ * Returns SD_EINVAL on a bad size or pointer, SD_ELAUNCH if the launch fails.
+ */
+long long sd_stream_read_sink_words(long long bytes);
+int sd_stream_read(hipStream_t stream, const void* src, long long bytes, uint32_t* sink);
 
 #ifdef __cplusplus
 }

@@ -98,6 +98,8 @@ def check_stats(gpu, ora, reqs, ell, gmax):
     for i, r in enumerate(reqs):
         L = int(ell[r])
         if ora["status"][i] & (OV.ST_NONFINITE | OV.ST_ZERO_Z):
+            if gpu.get("alpha") is not None:
+                assert np.all(to_np(gpu["alpha"])[r] == 0)   # a failed request accepts nothing
             continue
         assert_rel(rs[r, :L + 1, 0], ora["tgt_stats"][i, :L + 1, 0], what=f"r{r} target m", atol=REL)
         assert_rel(rs[r, :L + 1, 1], ora["tgt_stats"][i, :L + 1, 1], what=f"r{r} target Z")

@@ -104,3 +104,16 @@ def test_markov_host_validation():
     assert _mk(ws=8) == _lib.SD_ERANGE
     assert _mk(nulls=("C",)) == _lib.SD_EINVAL
     assert _mk(R=0) == _lib.SD_OK
+
+
+def test_stream_read_host_validation():
+    L = sdv.lib()
+    assert L.sd_stream_read_sink_words(0) == 0
+    assert L.sd_stream_read_sink_words(32768) == 1
+    assert L.sd_stream_read_sink_words(32784) == 2
+    assert L.sd_stream_read_sink_words(-16) == -1
+    p = ctypes.c_void_p(256)
+    assert L.sd_stream_read(None, p, 24, p) == _lib.SD_EINVAL        # not a multiple of 16
+    assert L.sd_stream_read(None, None, 32, p) == _lib.SD_EINVAL     # no source
+    assert L.sd_stream_read(None, ctypes.c_void_p(8), 32, p) == _lib.SD_EINVAL   # misaligned
+    assert L.sd_stream_read(None, p, 0, None) == _lib.SD_OK          # nothing to read

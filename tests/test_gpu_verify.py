@@ -64,6 +64,16 @@ def test_verify_ragged_vocab_and_padded_rows():
         _full_check(inp, ell)
 
 
+def test_verify_vocab_beyond_one_block_per_thread():
+    # V > 1024 blocks of 1024: each thread of the correction draw owns a run of
+    # two residual blocks; the last chunk and the last block are partial
+    for dtype in (torch.bfloat16, torch.float32):
+        inp = _to_cuda(verify_inputs(R=4, gmax=2, V=1_050_632, dtype=dtype, sigma_t=2.0,
+                                     zipf=True, sigma_d=(1.0, 3.0), seed=82))
+        ell = torch.tensor([2, 2, 1, 0], dtype=torch.int32, device="cuda")
+        _full_check(inp, ell)
+
+
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
