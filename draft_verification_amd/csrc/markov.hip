@@ -12,11 +12,15 @@
 //   k_markov_bias    the only dense contraction: G = A_k[x_{k-1}] . C_k as a
 //                    bf16 MFMA GEMM (M = requests, N = vocabulary, K = rank),
 //                    fused with + U_k, bf16 rounding, the q_logits store and a
-//                    per-(row, 128-column tile) partial (max, sum 2^(L*c - ref))
+//                    per-(row, 128-column tile) partial (max, sum 2^(L*c - ref));
+//                    the rows A_k[x_{k-1}] arrive pre-gathered, so every load
+//                    of a workgroup is issued before its first wait
 //   k_markov_select  one workgroup per request: confidence of position k,
 //                    combine tile partials, locate the inverse-CDF tile,
-//                    rescan 128 logits, emit x_k
-// plus one k_hidden_dot launch up front for w_h . h_k of every position.
+//                    rescan 128 logits, emit x_k, and gather A_{k+1}[x_k]
+//                    for the next step
+// plus, up front, one k_hidden_dot launch for w_h . h_k of every position and
+// one k_gather_a launch for A_1[x_0].
 #include "sdv_common.h"
 #include "sdv_host.h"
 
@@ -33,7 +37,34 @@ constexpr float kNegInf = -__builtin_huge_valf();
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Reductions over each 16-lane DPP row; every lane of the row gets the result.
+// Partners: xor 1, xor 2 (quad permutes), then the half-row and row mirrors.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
 __device__ __forceinline__ float exp_ref(float m, float c) { return m == kNegInf ? 0.0f : m * c; }
 
 // ---------------------------------------------------------------------------
@@ -59,21 +90,34 @@ __global__ __launch_bounds__(kThreads) void k_hidden_dot(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// G tile = A_k[x_prev[m0..m0+127]] (128 x rank) . Ct_k[n0..n0+127]^T (rank x 128)
+// Ag[r] = A_k[x_prev[r]] (rank bf16), zeros when x_prev is outside [0, V): the
+// anchor contributes no Markov bias.  Used for step 1; k_markov_select does it
+// for the following steps.
+__global__ __launch_bounds__(64) void k_gather_a(int R, int V, int rank, const uint16_t* __restrict__ Ak,
+                                                 const int32_t* __restrict__ xprev,
+                                                 uint16_t* __restrict__ Ag) {
+  const int r = blockIdx.x;
+  const int xp = xprev[r];
+  const bool valid = xp >= 0 && xp < V;
+  for (int v = threadIdx.x; v < rank / 8; v += 64)
+    ((uint4*)(Ag + (size_t)r * rank))[v] =
+        valid ? ((const uint4*)(Ak + (size_t)xp * rank))[v] : make_uint4(0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// G tile = Ag[m0..m0+127] (128 x rank) . Ct_k[n0..n0+127]^T (rank x 128)
 // with v_mfma_f32_16x16x32_bf16: wave w owns columns [32w, 32w+32) of the tile,
 // all 128 rows: 8 row blocks x 2 column blocks of 16 x 16 accumulators.
 __global__ __launch_bounds__(kThreads) void k_markov_bias(
     int R, int gamma, int k, int V, int rank, float c, const uint16_t* __restrict__ U,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Ct,
-    const int32_t* __restrict__ x0, const int32_t* __restrict__ tokens,
+    const uint16_t* __restrict__ Ct, const uint16_t* __restrict__ Ag,
     uint16_t* __restrict__ q_logits, float2* __restrict__ partial, int n_tiles) {
-  // LDS: gathered A rows during the GEMM, then the fp32 output tile.
+  // LDS: the A rows during the GEMM, then the fp32 output tile.
   constexpr int kAbytes = kTileM * (kMaxRank + kApad) * 2;
   constexpr int kGbytes = kTileM * (kTileN + kGpad) * 4;
   constexpr int kEpiPasses = kTileM / 16;
-  constexpr int kGatherPerThread = kTileM * (kMaxRank / 8) / kThreads;
+  constexpr int kAPerThread = kTileM * (kMaxRank / 8) / kThreads;
   __shared__ __align__(16) unsigned char lds[kAbytes > kGbytes ? kAbytes : kGbytes];
-  __shared__ int s_xp[kTileM];
   uint16_t* sA = (uint16_t*)lds;
   float* sG = (float*)lds;
 
@@ -83,17 +127,20 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
   const int m0 = blockIdx.y * kTileM;
   const int lda = rank + kApad;
   const int ksteps = rank / 32;
-  const size_t vr = (size_t)V * rank;
-  const uint16_t* Ak = A + (size_t)(k - 1) * vr;
-  const uint16_t* Ck = Ct + (size_t)(k - 1) * vr;
+  const uint16_t* Ck = Ct + (size_t)(k - 1) * V * rank;
 
-  // Every HBM read of the workgroup is issued up front so that their
-  // latencies overlap: previous tokens, B fragments, the U tile, the A rows.
-  if (tid < kTileM) {
-    const int r = m0 + tid;
-    int xp = -1;
-    if (r < R) xp = (k == 1) ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
-    s_xp[tid] = (xp >= 0 && xp < V) ? xp : -1;  // out of range: no Markov bias
+  // Every HBM read of the workgroup is issued before the first wait: the A
+  // rows (needed first), the B fragments, then the U tile for the epilogue.
+  const int vec_per_row = rank / 8;
+  const int total = kTileM * vec_per_row;
+  uint4 gat[kAPerThread];
+#pragma unroll
+  for (int i = 0; i < kAPerThread; ++i) {
+    const int idx = tid + i * kThreads;
+    const int row = idx / vec_per_row;
+    gat[i] = (idx < total && m0 + row < R)
+                 ? *(const uint4*)(Ag + (size_t)(m0 + row) * rank + (idx % vec_per_row) * 8)
+                 : make_uint4(0, 0, 0, 0);
   }
   // B fragments: lane l holds column (l % 16) of its 16-column block,
   // K values [32*ks + 8*(l/16), +8).
@@ -118,21 +165,8 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
     upre[pass] = (r < R && ecol < V) ? sdv::ld_nt(U + ((size_t)r * gamma + (k - 1)) * V + ecol)
                                      : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();  // s_xp
-  const int vec_per_row = rank / 8;
-  const int total = kTileM * vec_per_row;
-  uint4 gat[kGatherPerThread];
 #pragma unroll
-  for (int i = 0; i < kGatherPerThread; ++i) {
-    const int idx = tid + i * kThreads;
-    gat[i] = make_uint4(0, 0, 0, 0);
-    if (idx < total) {
-      const int xp = s_xp[idx / vec_per_row];
-      if (xp >= 0) gat[i] = *(const uint4*)(Ak + (size_t)xp * rank + (idx % vec_per_row) * 8);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kGatherPerThread; ++i) {
+  for (int i = 0; i < kAPerThread; ++i) {
     const int idx = tid + i * kThreads;
     if (idx < total) *(uint4*)(sA + (idx / vec_per_row) * lda + (idx % vec_per_row) * 8) = gat[i];
   }
@@ -173,43 +207,37 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
   __syncthreads();
 
   // Epilogue: L = bf16(U + G), stored; per-(row, tile) partial (max, sum).
+  // The 16 threads of a row are one DPP row of the wave.
 #pragma unroll
   for (int pass = 0; pass < kEpiPasses; ++pass) {
     const int mr = pass * 16 + (tid >> 4);
     const int r = m0 + mr;
-    float m = kNegInf, s = 0.0f;
-    float vals[8];
     const bool live = (r < R) && (ecol < V);
+    const uint4 u = upre[pass];
+    const float4 g0 = *(const float4*)(sG + mr * ldg + seg * 8);
+    const float4 g1 = *(const float4*)(sG + mr * ldg + seg * 8 + 4);
+    uint4 o;
+    o.x = pack_bf16_rne(sdv::bf16lo(u.x) + g0.x, sdv::bf16hi(u.x) + g0.y);
+    o.y = pack_bf16_rne(sdv::bf16lo(u.y) + g0.z, sdv::bf16hi(u.y) + g0.w);
+    o.z = pack_bf16_rne(sdv::bf16lo(u.z) + g1.x, sdv::bf16hi(u.z) + g1.y);
+    o.w = pack_bf16_rne(sdv::bf16lo(u.w) + g1.z, sdv::bf16hi(u.w) + g1.w);
+    const float vals[8] = {sdv::bf16lo(o.x), sdv::bf16hi(o.x), sdv::bf16lo(o.y), sdv::bf16hi(o.y),
+                           sdv::bf16lo(o.z), sdv::bf16hi(o.z), sdv::bf16lo(o.w), sdv::bf16hi(o.w)};
+    float m = kNegInf;
     if (live) {
-      const size_t off = ((size_t)r * gamma + (k - 1)) * V + ecol;
-      const uint4 u = upre[pass];
-      const float* g = sG + mr * ldg + seg * 8;
-      const float uu[8] = {sdv::bf16lo(u.x), sdv::bf16hi(u.x), sdv::bf16lo(u.y), sdv::bf16hi(u.y),
-                           sdv::bf16lo(u.z), sdv::bf16hi(u.z), sdv::bf16lo(u.w), sdv::bf16hi(u.w)};
-      uint16_t ob[8];
+      sdv::st_nt(q_logits + ((size_t)r * gamma + (k - 1)) * V + ecol, o);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ob[e] = sdv::f32_to_bf16_rne(uu[e] + g[e]);
-        vals[e] = sdv::bf16_to_f32(ob[e]);
-        m = fmaxf(m, vals[e]);
-      }
-      uint4 o;
-      o.x = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
-      o.y = (uint32_t)ob[2] | ((uint32_t)ob[3] << 16);
-      o.z = (uint32_t)ob[4] | ((uint32_t)ob[5] << 16);
-      o.w = (uint32_t)ob[6] | ((uint32_t)ob[7] << 16);
-      sdv::st_nt(q_logits + off, o);
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, vals[e]);
     }
     // row partial over the 16 lanes of this row: max, then sum relative to it
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    m = row16_max(m);
     const float ref = exp_ref(m, c);
+    float s = 0.0f;
     if (live) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += sdv::fast_exp2(fmaf(vals[e], c, -ref));
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+    s = row16_sum(s);
     if (seg == 0 && r < R) partial[(size_t)r * n_tiles + tile] = make_float2(m, s);
   }
 }
@@ -220,8 +248,9 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     const int64_t* __restrict__ pos0, const int32_t* __restrict__ x0,
     const uint16_t* __restrict__ E, const float* __restrict__ w,
     const float* __restrict__ hdot, const float2* __restrict__ partial, int n_tiles,
-    const uint16_t* __restrict__ q_logits, int32_t* __restrict__ tokens,
-    float* __restrict__ conf, int32_t* __restrict__ status) {
+    const uint16_t* __restrict__ q_logits, int rank, const uint16_t* __restrict__ A,
+    uint16_t* __restrict__ Ag, int32_t* __restrict__ tokens, float* __restrict__ conf,
+    int32_t* __restrict__ status) {
   __shared__ float s_red[kThreads / 64];
   __shared__ double s_redd[kThreads / 64];
   __shared__ int s_tile;
@@ -287,6 +316,9 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       tokens[(size_t)r * gamma + (k - 1)] = -1;
       status[r] = st | bad;
     }
+    if (k < gamma)  // no anchor for the next step: no Markov bias
+      for (int v = tid; v < rank / 8; v += kThreads)
+        ((uint4*)(Ag + (size_t)r * rank))[v] = make_uint4(0, 0, 0, 0);
     return;
   }
 
@@ -361,24 +393,32 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     if (lane == 0) s_tok = (found != 0x7FFFFFFF) ? found : lastm;
   }
   __syncthreads();
+  const int tok = s_tok;
   if (tid == 0) {
-    tokens[(size_t)r * gamma + (k - 1)] = s_tok;
+    tokens[(size_t)r * gamma + (k - 1)] = tok;
     status[r] = st;
+  }
+  if (k < gamma) {  // the next step's Markov rows: A_{k+1}[x_k]
+    const bool valid = tok >= 0 && tok < V;
+    const uint16_t* Anext = A + (size_t)k * V * rank;
+    for (int v = tid; v < rank / 8; v += kThreads)
+      ((uint4*)(Ag + (size_t)r * rank))[v] =
+          valid ? ((const uint4*)(Anext + (size_t)tok * rank))[v] : make_uint4(0, 0, 0, 0);
   }
 }
 
-size_t markov_ws_bytes(int R, int gamma, int V) {
+size_t markov_ws_bytes(int R, int gamma, int V, int rank) {
   const size_t n_tiles = ((size_t)V + kTileN - 1) / kTileN;
   return sdv_align256((size_t)R * gamma * sizeof(float)) +
-         sdv_align256((size_t)R * n_tiles * sizeof(float2));
+         sdv_align256((size_t)R * n_tiles * sizeof(float2)) +
+         sdv_align256((size_t)R * rank * sizeof(uint16_t));
 }
 
 }  // namespace
 
 extern "C" size_t sd_markov_draft_workspace_size(int R, int gamma, int V, int rank) {
-  (void)rank;
-  if (R < 0 || gamma < 0 || V <= 0) return 0;
-  return markov_ws_bytes(R, gamma, V);
+  if (R < 0 || gamma < 0 || V <= 0 || rank < 0) return 0;
+  return markov_ws_bytes(R, gamma, V, rank);
 }
 
 extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
@@ -398,7 +438,7 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
   if (R == 0 || gamma == 0) return SD_OK;
   if (!U || !A || !Ct || !x0 || !w || !tokens || !q_logits || !conf || !status) return SD_EINVAL;
   if ((H > 0 && !h) || (rank_e > 0 && !E)) return SD_EINVAL;
-  if (!workspace || workspace_bytes < markov_ws_bytes(R, gamma, V)) return SD_ERANGE;
+  if (!workspace || workspace_bytes < markov_ws_bytes(R, gamma, V, rank)) return SD_ERANGE;
   if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
   if ((((uintptr_t)U | (uintptr_t)A | (uintptr_t)Ct | (uintptr_t)q_logits | (uintptr_t)h |
         (uintptr_t)w) & 15) != 0)
@@ -409,6 +449,8 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
   float* hdot = (float*)p;
   p += sdv_align256((size_t)R * gamma * sizeof(float));
   float2* partial = (float2*)p;
+  p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
+  uint16_t* Ag = (uint16_t*)p;
 
   const int rows = R * gamma;
   if (H > 0) {
@@ -417,15 +459,15 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
   } else {
     return SD_EINVAL;  // the confidence head needs a hidden state
   }
+  SDV_TRY_LAUNCH(sdv::launch(k_gather_a, dim3(R), dim3(64), 0, stream, R, V, rank, A, x0, Ag));
   const dim3 grid_bias(n_tiles, (R + kTileM - 1) / kTileM);
   for (int k = 1; k <= gamma; ++k) {
     SDV_TRY_LAUNCH(sdv::launch(k_markov_bias, grid_bias, dim3(kThreads), 0, stream, R, gamma, k, V,
-                               rank, c, U, A, Ct, x0, (const int32_t*)tokens, q_logits, partial,
-                               n_tiles));
+                               rank, c, U, Ct, (const uint16_t*)Ag, q_logits, partial, n_tiles));
     SDV_TRY_LAUNCH(sdv::launch(k_markov_select, dim3(R), dim3(kThreads), 0, stream, gamma, k, V, H,
                                rank_e, c, seed, pos0, x0, E, w, (const float*)hdot,
-                               (const float2*)partial, n_tiles, (const uint16_t*)q_logits, tokens,
-                               conf, status));
+                               (const float2*)partial, n_tiles, (const uint16_t*)q_logits, rank, A,
+                               Ag, tokens, conf, status));
   }
   return SD_OK;
 }
