@@ -29,10 +29,23 @@ Readings of the pages (all listed in the design notes):
   * global argmax: the smallest n maximising Theta_n over n = 0..N;
   * capped top-K: exactly min(K, N) candidates.
 
+Two further modes of use (DSpark summary, "2.1 confidence head": sequential
+temperature scaling; experiments: confidence-threshold sweep):
+  * sequential temperature scaling (STS) recalibrates every confidence before
+    the survival products: c' = sigmoid(logit(c) / T_j) with one temperature
+    per draft position j, read as classic temperature scaling of a binary
+    probability; computed in fp64 as 1 / (1 + ((1 - c) / c) ** (1 / T_j)) and
+    rounded to fp32 (c = 0 stays 0, c = 1 stays 1);
+  * threshold mode keeps every candidate whose survival is at least theta:
+    l_r = max{j : a[r,j] >= theta} (survival never grows along j, so this is
+    the prefix of the sorted order with a >= theta).
+
 Pins: numpy.cumprod in fp32 for the survival (closed form), a brute-force
 search over every prefix-length vector for the global argmax, an independent
 frontier-greedy for the early stop, the constant-SPS special case and the
-Figure 1 construction (tests/test_oracle_schedule.py).
+Figure 1 construction; for STS scipy's expit/logit, the T = 1 identity and
+the symmetries of the sigmoid; for the threshold mode the per-request
+definition (tests/test_oracle_schedule.py).
 """
 
 import numpy as np
@@ -40,6 +53,7 @@ import numpy as np
 EARLY_STOP = 0
 GLOBAL_ARGMAX = 1
 CAPPED_TOPK = 2
+THRESHOLD = 3
 
 FIXED_POINT_SCALE = 2.0 ** 32
 
@@ -56,6 +70,25 @@ def survival(conf, gamma_r=None) -> np.ndarray:
             prod = np.float32(prod * conf[r, j])
             a[r, j] = prod
     return a
+
+
+def sts(conf, temps) -> np.ndarray:
+    """Sequential temperature scaling: c'[r, j] = fp32(sigmoid(logit(c[r, j]) / T[j]))."""
+    conf = np.asarray(conf, dtype=np.float32)
+    temps = np.asarray(temps, dtype=np.float64)
+    R, gmax = conf.shape
+    out = np.zeros((R, gmax), dtype=np.float32)
+    for r in range(R):
+        for j in range(gmax):
+            c = float(conf[r, j])
+            if c <= 0.0:
+                out[r, j] = 0.0
+            elif c >= 1.0:
+                out[r, j] = 1.0
+            else:
+                odds = (1.0 - c) / c        # exp(-logit(c))
+                out[r, j] = np.float32(1.0 / (1.0 + odds ** (1.0 / temps[j])))
+    return out
 
 
 def fixed_point(a: float) -> int:
@@ -88,14 +121,18 @@ def theta_curve(order, R, sps):
     return thetas, taus
 
 
-def schedule(conf, sps, mode=EARLY_STOP, gamma_r=None, cap_k=None):
+def schedule(conf, sps, mode=EARLY_STOP, gamma_r=None, cap_k=None, threshold=None,
+             sts_temp=None):
     """Choose per-request verify lengths l_r.
 
     Returns a dict: ell[R] (int32), B, n_sel, theta (fp64 Theta at the chosen
     point), surv[R][gamma_max] (fp32), order (the sorted candidate list) and
-    thetas (the Theta curve, n = 0..N).
+    thetas (the Theta curve, n = 0..N).  sts_temp[gamma_max], if given,
+    recalibrates the confidences first.
     """
     conf = np.asarray(conf, dtype=np.float32)
+    if sts_temp is not None:
+        conf = sts(conf, sts_temp)
     R, gmax = conf.shape
     g = np.full(R, gmax, dtype=np.int64) if gamma_r is None else np.asarray(gamma_r, np.int64)
     sps = np.asarray(sps, dtype=np.float32)
@@ -121,6 +158,10 @@ def schedule(conf, sps, mode=EARLY_STOP, gamma_r=None, cap_k=None):
         if cap_k is None:
             raise ValueError("capped mode needs K")
         n_sel = min(max(int(cap_k), 0), N)
+    elif mode == THRESHOLD:
+        if threshold is None:
+            raise ValueError("threshold mode needs theta")
+        n_sel = sum(1 for (a_, _r, _j) in order if a_ >= np.float32(threshold))
     else:
         raise ValueError("unknown mode")
 

@@ -198,3 +198,60 @@ def test_figure1_construction():
     res = S.schedule(conf, sps, S.EARLY_STOP)
     assert list(res["ell"]) == case["expected_ell"]
     assert res["B"] == case["expected_B"]
+
+
+# --- sequential temperature scaling and the threshold mode -------------------
+
+def test_sts_matches_expit_of_scaled_logit():
+    from scipy.special import expit, logit
+    g = np.random.default_rng(11)
+    conf = g.uniform(0.001, 0.999, (6, 7)).astype(np.float32)
+    temps = g.uniform(0.3, 3.0, 7)
+    got = S.sts(conf, temps).astype(np.float64)
+    want = expit(logit(conf.astype(np.float64)) / temps[None, :])
+    assert np.allclose(got, want, rtol=2 ** -23, atol=0)
+
+
+def test_sts_identity_symmetry_and_limits():
+    g = np.random.default_rng(12)
+    conf = g.uniform(0.0, 1.0, (5, 4)).astype(np.float32)
+    conf[0, 0], conf[0, 1], conf[1, 0] = 0.0, 1.0, 0.5
+    assert np.array_equal(S.sts(conf, np.ones(4)), conf)           # T = 1: unchanged, bit for bit
+    t = np.array([0.5, 2.0, 7.0, 0.25])
+    out = S.sts(conf, t)
+    assert out[0, 0] == 0.0 and out[0, 1] == 1.0 and out[1, 0] == 0.5
+    mirrored = S.sts((1.0 - conf.astype(np.float64)).astype(np.float32), t)
+    inner = (conf > 0) & (conf < 1) & (np.abs(1.0 - conf.astype(np.float64) - (1.0 - conf)) == 0)
+    assert np.allclose(mirrored[inner], 1.0 - out[inner], atol=1e-7)   # sigma(-z) = 1 - sigma(z)
+    big = S.sts(conf, np.full(4, 1e6))
+    inner = (conf > 0) & (conf < 1)
+    assert np.allclose(big[inner], 0.5, atol=1e-5)                       # T -> inf: 1/2
+    # a temperature above 1 pulls every confidence toward 1/2, below 1 away from it
+    hot, cold = S.sts(conf, np.full(4, 2.0)), S.sts(conf, np.full(4, 0.5))
+    d = np.abs(conf - 0.5)
+    assert np.all(np.abs(hot - 0.5)[inner] <= d[inner] + 1e-7)
+    assert np.all(np.abs(cold - 0.5)[inner] >= d[inner] - 1e-7)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_threshold_mode_is_the_per_request_definition(seed):
+    g = np.random.default_rng(100 + seed)
+    conf, gam, sps = _rand_case(g, 9, 6, ragged=True, levels=[0.3, 0.6, 0.9, 1.0] if seed == 2 else None)
+    a = S.survival(conf, gam)
+    for theta in (0.0, 0.05, 0.3, float(a[0, 0]), 0.81, 1.0, 1.5):
+        res = S.schedule(conf, sps, S.THRESHOLD, gam, threshold=theta)
+        for r in range(9):
+            js = [j for j in range(1, gam[r] + 1) if a[r, j - 1] >= np.float32(theta)]
+            assert res["ell"][r] == (max(js) if js else 0)
+            assert js == list(range(1, len(js) + 1))                     # a prefix of the draft
+        assert res["B"] == 9 + int(res["ell"].sum())
+
+
+def test_sts_applies_before_the_survival_products():
+    g = np.random.default_rng(13)
+    conf, gam, sps = _rand_case(g, 5, 5)
+    temps = g.uniform(0.5, 2.0, 5)
+    res = S.schedule(conf, sps, S.GLOBAL_ARGMAX, gam, sts_temp=temps)
+    assert np.array_equal(res["surv"], S.survival(S.sts(conf, temps), gam))
+    plain = S.schedule(S.sts(conf, temps), sps, S.GLOBAL_ARGMAX, gam)
+    assert np.array_equal(res["ell"], plain["ell"]) and res["theta"] == plain["theta"]
