@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     SD_SCHED_EARLY_STOP,
     SD_SCHED_GLOBAL_ARGMAX,
     SD_SCHED_CAPPED_TOPK,
+    SD_SCHED_THRESHOLD,
     SD_ST_BAD_TOKEN,
     SD_ST_NONFINITE,
     SD_ST_ZERO_Z,

@@ -26,6 +26,7 @@ SD_DTYPE_BF16 = 1
 SD_SCHED_EARLY_STOP = 0
 SD_SCHED_GLOBAL_ARGMAX = 1
 SD_SCHED_CAPPED_TOPK = 2
+SD_SCHED_THRESHOLD = 3
 
 SD_ST_BAD_TOKEN = 1
 SD_ST_NONFINITE = 2
@@ -68,7 +69,8 @@ def lib():
     L.sd_schedule.restype = _I
     L.sd_schedule_workspace_size.restype = _SZ
     L.sd_schedule_workspace_size.argtypes = [_I, _I]
-    L.sd_schedule.argtypes = [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ]
+    L.sd_schedule.argtypes = [_P, _I, _I, _P, _P, _P, _P, _I, _I, _P, ctypes.c_float, _P, _P, _P,
+                              _P, _P, _P, _SZ]
     L.sd_verify_workspace_size.restype = _SZ
     L.sd_verify_workspace_size.argtypes = [_I, _I, _I]
     L.sd_verify.restype = _I
@@ -132,10 +134,12 @@ def sd_schedule_workspace_size(R, gmax):
 
 
 def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, workspace=None,
-                stream=None):
+                stream=None, sts_temp=None, threshold=0.0):
     """Run the scheduler.  conf [R][gmax] fp32, sps fp32, gamma_r [R] int32 or
-    None, cap_k a 1-element int32 device tensor (CAPPED_TOPK).  Returns a dict
-    of device tensors: ell, batch, n_sel, theta, surv."""
+    None, cap_k a 1-element int32 device tensor (CAPPED_TOPK), sts_temp
+    [gmax] fp32 per-position temperatures or None, threshold the survival
+    threshold (THRESHOLD mode).  Returns a dict of device tensors: ell, batch,
+    n_sel, theta, surv."""
     R, gmax = conf.shape
     dev = conf.device
     o = out or {}
@@ -147,8 +151,9 @@ def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, 
     ws = workspace if workspace is not None else _workspace(sd_schedule_workspace_size(R, gmax), dev)
     code = lib().sd_schedule(
         _stream(stream), R, gmax, _ptr(gamma_r, torch.int32, "gamma_r"),
-        _ptr(conf, torch.float32, "conf"), _ptr(sps, torch.float32, "sps"), sps.numel(), int(mode),
-        _ptr(cap_k, torch.int32, "cap_k"), _ptr(ell, torch.int32), _ptr(batch, torch.int32),
+        _ptr(conf, torch.float32, "conf"), _ptr(sts_temp, torch.float32, "sts_temp"),
+        _ptr(sps, torch.float32, "sps"), sps.numel(), int(mode), _ptr(cap_k, torch.int32, "cap_k"),
+        float(threshold), _ptr(ell, torch.int32), _ptr(batch, torch.int32),
         _ptr(n_sel, torch.int32), _ptr(theta, torch.float64), _ptr(sv, torch.float32),
         ws.data_ptr(), ws.numel())
     _check("sd_schedule", code)

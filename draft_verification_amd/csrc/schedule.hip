@@ -7,6 +7,11 @@
 // history page, DSpark "move two": a_{r,j} is the product of the per-position
 // confidences up to j.
 //
+// Optional sequential temperature scaling (DSpark summary, "2.1 confidence
+// head"): c' = sigmoid(logit(c) / T_j) per draft position j, in fp64 rounded
+// to fp32, before the products.  Threshold mode (the confidence-threshold
+// sweep of the same page) keeps every candidate whose survival is >= theta.
+//
 // Keys are uint64 so that one ascending integer order sorts by survival
 // descending, then request, then position; they are unique.  Two kernels:
 //   k_sched_rank    many workgroups: each rebuilds every key in LDS (one
@@ -39,6 +44,15 @@ __device__ __forceinline__ float key_survival(uint64_t key) {
 // q = rint(a * 2^32): exact in fp64 (a has 24 significant bits).
 __device__ __forceinline__ uint64_t key_fixed_point(uint64_t key) {
   return (uint64_t)__builtin_rint((double)key_survival(key) * 4294967296.0);
+}
+
+// c' = 1 / (1 + ((1 - c) / c)^(1 / T)) = sigmoid(logit(c) / T); 0 and 1 are fixed.
+__device__ __forceinline__ float sts_calibrate(float c, float T) {
+  if (c != c) return c;  // NaN stays NaN
+  if (!(c > 0.0f)) return 0.0f;
+  if (c >= 1.0f) return 1.0f;
+  const double odds = (1.0 - (double)c) / (double)c;
+  return (float)(1.0 / (1.0 + pow(odds, 1.0 / (double)T)));
 }
 
 __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, int lane) {
@@ -75,13 +89,18 @@ __device__ __forceinline__ void request_keys(int r, int gmax, const int32_t* gam
 
 __global__ __launch_bounds__(kRankThreads) void k_sched_rank(
     int R, int gmax, const int32_t* __restrict__ gamma_r, const float* __restrict__ conf,
-    float* __restrict__ surv, uint64_t* __restrict__ sorted) {
+    const float* __restrict__ sts_temp, float* __restrict__ surv, uint64_t* __restrict__ sorted) {
   extern __shared__ uint64_t keys[];
   __shared__ int part[kRankSegs][kRankCand];
   const int tid = threadIdx.x;
   const int nslots = R * gmax;
   float* my_surv = blockIdx.x == 0 ? surv : nullptr;  // one workgroup writes it
-  for (int i = tid; i < nslots; i += kRankThreads) keys[i] = __float_as_uint(conf[i]);  // coalesced
+  if (sts_temp) {
+    for (int i = tid; i < nslots; i += kRankThreads)
+      keys[i] = __float_as_uint(sts_calibrate(conf[i], sts_temp[i % gmax]));
+  } else {
+    for (int i = tid; i < nslots; i += kRankThreads) keys[i] = __float_as_uint(conf[i]);  // coalesced
+  }
   __syncthreads();
   for (int r = tid; r < R; r += kRankThreads) request_keys(r, gmax, gamma_r, keys, my_surv);
   __syncthreads();
@@ -113,12 +132,12 @@ __global__ __launch_bounds__(kRankThreads) void k_sched_rank(
 template <int E>
 __global__ __launch_bounds__(kThreads) void k_sched_select(
     int R, int gmax, const int32_t* __restrict__ gamma_r, const float* __restrict__ sps,
-    int mode, const int32_t* __restrict__ cap_k, const uint64_t* __restrict__ sorted,
+    int mode, const int32_t* __restrict__ cap_k, float threshold, const uint64_t* __restrict__ sorted,
     int32_t* __restrict__ ell, int32_t* __restrict__ batch_out, int32_t* __restrict__ n_sel_out,
     double* __restrict__ theta_out) {
   __shared__ int ell_lds[SD_MAX_SCHED_SLOTS];
   __shared__ uint64_t wave_tot[kWaves];
-  __shared__ int s_count, s_fail, s_nstar;
+  __shared__ int s_count, s_fail, s_nstar, s_above;
   __shared__ double s_best_theta[kWaves];
   __shared__ int s_best_n[kWaves];
 
@@ -136,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
     sps_n[e] = i < nslots ? sps[R + i] : 0.0f;
   }
   sps_prev = (i0 >= 1 && i0 - 1 < nslots) ? sps[R + i0 - 1] : 0.0f;
-  if (tid == 0) { s_count = 0; s_fail = 0x7FFFFFFF; }
+  if (tid == 0) { s_count = 0; s_fail = 0x7FFFFFFF; s_above = 0; }
   __syncthreads();
   int my_count = 0;
   for (int r = tid; r < R; r += kThreads) {
@@ -184,6 +203,13 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
       if (th > best) { best = th; best_n = n; }
     }
   }
+  if (mode == SD_SCHED_THRESHOLD) {  // candidates with survival >= theta (a prefix)
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (i0 + e < N && key_survival(key[e]) >= threshold) ++above;
+    if (above) atomicAdd(&s_above, above);
+  }
   fail = sdv::wave_min_i(fail);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -208,6 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
     int nstar;
     if (mode == SD_SCHED_EARLY_STOP) nstar = (s_fail == 0x7FFFFFFF) ? N : s_fail - 1;
     else if (mode == SD_SCHED_GLOBAL_ARGMAX) nstar = bn;
+    else if (mode == SD_SCHED_THRESHOLD) nstar = s_above;
     else nstar = sdv::clampi(*cap_k, 0, N);
     s_nstar = nstar;
     if (batch_out) *batch_out = R + nstar;
@@ -249,15 +276,18 @@ extern "C" size_t sd_schedule_workspace_size(int R, int gamma_max) {
 }
 
 extern "C" int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r,
-                           const float* conf, const float* sps, int sps_len, int mode,
-                           const int32_t* cap_k, int32_t* ell, int32_t* batch, int32_t* n_sel,
-                           double* theta, float* surv, void* workspace, size_t workspace_bytes) {
+                           const float* conf, const float* sts_temp, const float* sps, int sps_len,
+                           int mode, const int32_t* cap_k, float threshold, int32_t* ell,
+                           int32_t* batch, int32_t* n_sel, double* theta, float* surv,
+                           void* workspace, size_t workspace_bytes) {
   if (R < 0 || gamma_max < 0) return SD_EINVAL;
   if (gamma_max > SD_MAX_GAMMA) return SD_EUNSUPPORTED;
   if ((long long)R * gamma_max > SD_MAX_SCHED_SLOTS) return SD_EUNSUPPORTED;
-  if (mode != SD_SCHED_EARLY_STOP && mode != SD_SCHED_GLOBAL_ARGMAX && mode != SD_SCHED_CAPPED_TOPK)
+  if (mode != SD_SCHED_EARLY_STOP && mode != SD_SCHED_GLOBAL_ARGMAX &&
+      mode != SD_SCHED_CAPPED_TOPK && mode != SD_SCHED_THRESHOLD)
     return SD_EINVAL;
   if (mode == SD_SCHED_CAPPED_TOPK && !cap_k) return SD_EINVAL;
+  if (mode == SD_SCHED_THRESHOLD && threshold != threshold) return SD_EINVAL;  // NaN
   if (R > 0 && (!ell || !sps || (gamma_max > 0 && !conf))) return SD_EINVAL;
   if ((long long)sps_len < (long long)R * (1 + gamma_max)) return SD_ERANGE;
   if (!workspace || workspace_bytes < sched_ws_bytes(R, gamma_max)) return SD_ERANGE;
@@ -270,15 +300,16 @@ extern "C" int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32
       SDV_TRY_LAUNCH(hipFuncSetAttribute((const void*)k_sched_rank,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     SDV_TRY_LAUNCH(sdv::launch(k_sched_rank, dim3((nslots + kRankCand - 1) / kRankCand),
-                               dim3(kRankThreads), lds, stream, R, gamma_max, gamma_r, conf, surv,
-                               sorted));
+                               dim3(kRankThreads), lds, stream, R, gamma_max, gamma_r, conf,
+                               sts_temp, surv, sorted));
   }
   int npad = 1;
   while (npad < nslots) npad <<= 1;
   const int E = npad > kThreads ? npad / kThreads : 1;
 #define SDV_SELECT_LAUNCH(EV)                                                                   \
   SDV_TRY_LAUNCH(sdv::launch(k_sched_select<EV>, dim3(1), dim3(kThreads), 0, stream, R, gamma_max, \
-                             gamma_r, sps, mode, cap_k, (const uint64_t*)sorted, ell, batch, n_sel, \
+                             gamma_r, sps, mode, cap_k, threshold, (const uint64_t*)sorted, ell,   \
+                             batch, n_sel,                                                       \
                              theta))
   switch (E) {
     case 1: SDV_SELECT_LAUNCH(1); break;

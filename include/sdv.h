@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 1
+#define SDV_ABI_VERSION 2
 
 /* return codes (host side) */
 #define SD_OK             0
@@ -73,6 +73,7 @@ extern "C" {
 #define SD_SCHED_EARLY_STOP     0
 #define SD_SCHED_GLOBAL_ARGMAX  1
 #define SD_SCHED_CAPPED_TOPK    2
+#define SD_SCHED_THRESHOLD      3
 
 /* per-request device status bits */
 #define SD_ST_BAD_TOKEN      1   /* token id outside [0, V) */
@@ -95,6 +96,10 @@ const char* sd_status_string(int code);
 /*
  * sd_schedule - hardware-aware prefix scheduler [DS 2.2; SD move two/three].
  *
+ * If sts_temp is given, every confidence is first recalibrated by sequential
+ * temperature scaling [DS 2.1]: c' = sigmoid(logit(c) / sts_temp[j-1]) for
+ * draft position j, computed in fp64 as 1 / (1 + ((1-c)/c)^(1/T)) and rounded
+ * to fp32 (c <= 0 gives 0, c >= 1 gives 1, NaN stays NaN).
  * Survival a[r][j] = prod_{i<=j} conf[r][i] (fp32, left to right) is the
  * chance that request r's draft prefix up to position j is accepted.  All
  * candidates (r, j), j = 1..gamma_r[r], are ordered by survival descending,
@@ -111,6 +116,9 @@ const char* sd_status_string(int code);
  *                       before these confidences were known [DS challenge 2];
  *                       pass a previous GLOBAL_ARGMAX call's n_sel pointer as
  *                       cap_k to chain the two without a host round trip.
+ *   mode THRESHOLD:     n* = number of candidates with a >= threshold, i.e.
+ *                       ell[r] = max{j : a[r][j] >= threshold} [DS
+ *                       confidence-threshold sweep]; Theta_{n*} is reported.
  * Then ell[r] = number of selected candidates of request r, batch = R + n*.
  *
  *   R          requests, >= 0;   gamma_max in [0, SD_MAX_GAMMA];
@@ -118,9 +126,11 @@ const char* sd_status_string(int code);
  *   gamma_r    [R] int32 drafted length per request, clamped to
  *              [0, gamma_max]; NULL means gamma_max for all
  *   conf       [R][gamma_max] fp32 confidences in [0, 1] (finite)
+ *   sts_temp   [gamma_max] fp32 per-position temperatures (> 0) or NULL
  *   sps        [sps_len] fp32 throughput table, sps[B-1] for batch B;
  *              sps_len >= R * (1 + gamma_max) else SD_ERANGE
  *   cap_k      [1] int32, read in CAPPED_TOPK mode only (device)
+ *   threshold  survival threshold, used in THRESHOLD mode only (not NaN)
  *   ell        [R] int32 out
  *   batch, n_sel  [1] int32 out or NULL;  theta [1] fp64 out (Theta_{n*}) or NULL
  *   surv       [R][gamma_max] fp32 out or NULL: a[r][j-1], 0 past gamma_r
@@ -131,8 +141,9 @@ const char* sd_status_string(int code);
  */
 size_t sd_schedule_workspace_size(int R, int gamma_max);
 int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r,
-                const float* conf, const float* sps, int sps_len, int mode,
-                const int32_t* cap_k, int32_t* ell, int32_t* batch, int32_t* n_sel,
+                const float* conf, const float* sts_temp, const float* sps, int sps_len,
+                int mode, const int32_t* cap_k, float threshold, int32_t* ell,
+                int32_t* batch, int32_t* n_sel,
                 double* theta, float* surv, void* workspace, size_t workspace_bytes);
 
 /*

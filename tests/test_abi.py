@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sdv.sd_abi_version() == 1
+    assert sdv.sd_abi_version() == 2
     assert sdv.sd_status_string(0) == "ok"
     for code in (-1, -2, -3, -4, 1, 2, 4, 8, 16):
         assert sdv.sd_status_string(code) != "unknown status"
@@ -46,18 +46,19 @@ def test_workspace_sizes():
 N = None
 
 
-def _sched(R, g, mode, sps_len, conf=1, sps=1, ell=1, cap=None, ws=1 << 20):
+def _sched(R, g, mode, sps_len, conf=1, sps=1, ell=1, cap=None, ws=1 << 20, threshold=0.5):
     L = sdv.lib()
     p = lambda x: ctypes.c_void_p(16) if x else None
-    return L.sd_schedule(None, R, g, None, p(conf), p(sps), sps_len, mode, p(cap), p(ell), N, N, N, N,
-                         ctypes.c_void_p(256), ws)
+    return L.sd_schedule(None, R, g, None, p(conf), None, p(sps), sps_len, mode, p(cap), threshold,
+                         p(ell), N, N, N, N, ctypes.c_void_p(256), ws)
 
 
 def test_schedule_host_validation():
     assert _sched(-1, 4, 0, 100) == _lib.SD_EINVAL
     assert _sched(4, 256, 0, 10000) == _lib.SD_EUNSUPPORTED
     assert _sched(2048, 16, 0, 40000) == _lib.SD_EUNSUPPORTED      # 32768 slots
-    assert _sched(4, 4, 3, 100) == _lib.SD_EINVAL                  # bad mode
+    assert _sched(4, 4, 4, 100) == _lib.SD_EINVAL                  # bad mode
+    assert _sched(4, 4, 3, 100, threshold=float("nan")) == _lib.SD_EINVAL   # NaN threshold
     assert _sched(4, 4, 2, 100) == _lib.SD_EINVAL                  # capped without cap_k
     assert _sched(4, 4, 0, 19) == _lib.SD_ERANGE                   # table < R(1+g)
     assert _sched(4, 4, 0, 20, ell=0) == _lib.SD_EINVAL

@@ -14,21 +14,23 @@ pytestmark = pytest.mark.gpu
 MODES = [OS.EARLY_STOP, OS.GLOBAL_ARGMAX]
 
 
-def _run(conf, sps, mode, gamma_r=None, cap=None):
+def _run(conf, sps, mode, gamma_r=None, cap=None, threshold=0.0, sts=None):
     dev = "cuda"
     c = torch.as_tensor(conf, dtype=torch.float32).to(dev).contiguous()
     s = torch.as_tensor(sps, dtype=torch.float32).to(dev)
     g = None if gamma_r is None else torch.as_tensor(gamma_r, dtype=torch.int32).to(dev)
     k = None if cap is None else torch.tensor([int(cap)], dtype=torch.int32, device=dev)
-    out = sdv.sd_schedule(c, s, mode, gamma_r=g, cap_k=k)
+    t = None if sts is None else torch.as_tensor(sts, dtype=torch.float32).to(dev)
+    out = sdv.sd_schedule(c, s, mode, gamma_r=g, cap_k=k, threshold=threshold, sts_temp=t)
     torch.cuda.synchronize()
     return {k2: (v.cpu().numpy() if v is not None else None) for k2, v in out.items()}
 
 
-def _check(conf, sps, mode, gamma_r=None, cap=None):
+def _check(conf, sps, mode, gamma_r=None, cap=None, threshold=0.0, sts=None):
     conf = np.asarray(conf, np.float32)
-    got = _run(conf, sps, mode, gamma_r, cap)
-    ref = OS.schedule(conf, sps, mode, gamma_r, cap_k=cap)
+    got = _run(conf, sps, mode, gamma_r, cap, threshold, sts)
+    ref = OS.schedule(conf, sps, mode, gamma_r, cap_k=cap, threshold=threshold,
+                      sts_temp=None if sts is None else np.asarray(sts, np.float32))
     assert np.array_equal(got["ell"], ref["ell"]), (got["ell"], ref["ell"])
     assert int(got["batch"][0]) == ref["B"]
     assert int(got["n_sel"][0]) == ref["n_sel"]
@@ -110,3 +112,51 @@ def test_schedule_host_errors():
         sdv.sd_schedule(c, torch.ones(20, device=dev), 7)
     with pytest.raises(sdv.SdvError):
         sdv.sd_schedule(c, torch.ones(20, device=dev), OS.CAPPED_TOPK)  # no cap_k
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "headline"])
+def test_schedule_threshold_mode(name):
+    inp = verify_config(name, device="cpu", V=64)
+    conf, sps = inp["conf"].numpy(), inp["sps"].numpy()
+    a = OS.survival(conf)
+    for theta in (0.0, 0.1, 0.5, float(np.median(a)), float(a.max()), 1.0, 2.0, -1.0):
+        _check(conf, sps, OS.THRESHOLD, threshold=theta)
+
+
+def test_schedule_threshold_ragged_with_ties():
+    g = np.random.default_rng(14)
+    for case in range(20):
+        R, gmax = int(g.integers(1, 40)), int(g.integers(1, 17))
+        conf = g.choice(np.array([0.25, 0.5, 0.75, 1.0], np.float32), (R, gmax))
+        gam = g.integers(0, gmax + 1, R).astype(np.int32)
+        sps = g.uniform(0.5, 2.0, R * (gmax + 1)).astype(np.float32)
+        for theta in (0.25 ** 3, 0.5, 0.5625, 0.75):   # exactly representable survivals
+            _check(conf, sps, OS.THRESHOLD, gam, threshold=theta)
+
+
+def test_schedule_sts_every_mode():
+    """Sequential temperature scaling before the products: calibrated
+    survivals and every selection bit-identical to the oracle's."""
+    g = np.random.default_rng(15)
+    inp = verify_config("headline", device="cpu", V=64)
+    conf, sps = inp["conf"].numpy(), inp["sps"].numpy()
+    gmax = conf.shape[1]
+    temps = g.uniform(0.6, 2.5, gmax).astype(np.float32)
+    for mode in MODES:
+        _check(conf, sps, mode, sts=temps)
+    _check(conf, sps, OS.THRESHOLD, threshold=0.3, sts=temps)
+    _check(conf, sps, OS.CAPPED_TOPK, cap=1000, sts=temps)
+
+
+def test_schedule_sts_limits_and_identity():
+    g = np.random.default_rng(16)
+    R, gmax = 37, 9
+    conf = g.uniform(0.0, 1.0, (R, gmax)).astype(np.float32)
+    conf[0, :3] = (0.0, 1.0, 0.5)
+    gam = g.integers(0, gmax + 1, R).astype(np.int32)
+    sps = g.uniform(0.5, 2.0, R * (gmax + 1)).astype(np.float32)
+    for temps in (np.ones(gmax), np.full(gmax, 1e-3), np.full(gmax, 1e3), g.uniform(0.1, 10, gmax)):
+        _check(conf, sps, OS.GLOBAL_ARGMAX, gam, sts=temps.astype(np.float32))
+    ident = _run(conf, sps, OS.GLOBAL_ARGMAX, gam, sts=np.ones(gmax, np.float32))
+    plain = _run(conf, sps, OS.GLOBAL_ARGMAX, gam)
+    assert np.array_equal(ident["surv"], plain["surv"])   # T = 1 changes nothing
