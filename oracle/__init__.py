@@ -19,9 +19,12 @@ Sources (cited by page title and section):
   * speculative-decoding history page: "1.1 mechanism" (draft, parallel verify,
     rejection sampling, losslessness), DSpark "move one" (Markov head) and
     "move two / move three" (survival products, greedy scheduler).
-  * LightSpec article: "reserving token slots at the maximum draft length".
+  * LightSpec article: the two-stage budget planner (verify budget, then draft
+    budget), runtime statistics kept as EMAs with interpolation across draft
+    lengths, runtime cost tables; reserving token slots at the maximum draft
+    length.
 
 Parity status per function is stated in each module header.
 """
 
-from . import rng, schedule, verify, markov, bf16  # noqa: F401
+from . import rng, schedule, verify, markov, bf16, lightspec  # noqa: F401
