@@ -154,6 +154,54 @@ def bench_early_stop(sdv, torch, sets, bufs, ws, sws, steps):
             "note": "the chosen rows of both input sets fit in the 256 MB last-level cache"}
 
 
+def graph_time_us(torch, fn, calls=10, replays=10):
+    """Average time of fn() from a captured graph (the calls are shorter than
+    the host's per-call overhead)."""
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        fn()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(calls):
+                fn()
+    torch.cuda.current_stream().wait_stream(cap)
+    graph.replay()   # the first replay uploads the graph
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (calls * replays) * 1e3
+
+
+def bench_planner(sdv, torch, inp, vo, ell):
+    """Two-stage budget planner at the headline size: fold the step's
+    acceptance rates into the EMA table, then plan both budgets."""
+    R, G = inp["R"], inp["gmax"]
+    dev = "cuda"
+    alpha = torch.rand((R, G), device=dev)
+    ema = torch.full((G,), 0.5, dtype=torch.float64, device=dev)
+    cnt = torch.zeros(G, dtype=torch.int64, device=dev)
+    cost = torch.full((G,), 1e-5, device=dev)
+    out = dict(conf=torch.empty(G, device=dev), ell=torch.empty(R, dtype=torch.int32, device=dev),
+               batch=torch.empty(1, dtype=torch.int32, device=dev),
+               n_sel=torch.empty(1, dtype=torch.int32, device=dev),
+               theta=torch.empty(1, dtype=torch.float64, device=dev),
+               d_next=torch.empty(1, dtype=torch.int32, device=dev),
+               b_next=torch.empty(1, dtype=torch.int32, device=dev),
+               phi=torch.empty(G, dtype=torch.float64, device=dev))
+    ws = torch.empty(max(sdv.lib().sd_lightspec_plan_workspace_size(R, G), 256), dtype=torch.uint8,
+                     device=dev)
+    upd = lambda: sdv.sd_lightspec_update(alpha, ell, vo["status"], 0.1, ema, cnt)
+    pln = lambda: sdv.sd_lightspec_plan(ema, cnt, ell, inp["sps"], cost, out=out, workspace=ws)
+    return {"workload": f"R={R}, gamma={G}", "update_us": round(graph_time_us(torch, upd), 2),
+            "plan_us": round(graph_time_us(torch, pln), 2), "launches": 5}
+
+
 def bench_markov(sdv, torch, steps, hip):
     from workloads import markov_config
     inp = markov_config(device="cuda")
@@ -282,27 +330,9 @@ def main():
     # schedule alone (the rest of the step is verification): its kernels are
     # shorter than the host's per-call overhead, so time a captured graph
     so = bufs[0][0]
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        sdv.sd_schedule(sets[0]["conf"], sets[0]["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so, workspace=sws)
-        with torch.cuda.graph(graph, stream=cap):
-            for _ in range(10):
-                sdv.sd_schedule(sets[0]["conf"], sets[0]["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so,
-                                workspace=sws)
-    torch.cuda.current_stream().wait_stream(cap)
-    torch.cuda.synchronize()
-    graph.replay()   # the first replay uploads the graph
-    torch.cuda.synchronize()
-    s0 = torch.cuda.Event(enable_timing=True)
-    s1 = torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(10):
-        graph.replay()
-    s1.record()
-    torch.cuda.synchronize()
-    sched_us = s0.elapsed_time(s1) / 100 * 1e3
+    sched_us = graph_time_us(torch, lambda: sdv.sd_schedule(sets[0]["conf"], sets[0]["sps"],
+                                                            sdv.SD_SCHED_GLOBAL_ARGMAX, out=so,
+                                                            workspace=sws))
 
     # practical read ceiling: a plain streaming read of a buffer of the batch's
     # size with the bandwidth pass's load shape (two buffers alternate)
@@ -357,6 +387,8 @@ def main():
         "breakdown_us": {"step": round(ms_per_step * 1e3, 1), "schedule": round(sched_us, 1),
                          "row_stats_kernel": round(k_avg * 1e3, 1)},
     }
+    print("budget planner", file=sys.stderr, flush=True)
+    result["budget_planner"] = bench_planner(sdv, torch, sets[0], bufs[0][1], bufs[0][0]["ell"])
     if not args.no_early_stop:
         print("early-stop schedule", file=sys.stderr, flush=True)
         result["early_stop_block"] = bench_early_stop(sdv, torch, sets, bufs, ws, sws, K)

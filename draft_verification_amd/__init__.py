@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     sd_markov_draft,
     sd_markov_draft_workspace_size,
     sd_stream_read,
+    sd_lightspec_update,
+    sd_lightspec_plan,
     SD_SCHED_EARLY_STOP,
     SD_SCHED_GLOBAL_ARGMAX,
     SD_SCHED_CAPPED_TOPK,

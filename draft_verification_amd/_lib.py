@@ -38,6 +38,7 @@ EXPORTS = (
     "sd_abi_version", "sd_status_string", "sd_schedule_workspace_size", "sd_schedule",
     "sd_verify_workspace_size",
     "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
+    "sd_lightspec_update", "sd_lightspec_plan_workspace_size", "sd_lightspec_plan",
     "sd_stream_read_sink_words", "sd_stream_read",
 )
 
@@ -81,6 +82,13 @@ def lib():
     L.sd_markov_draft.restype = _I
     L.sd_markov_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P,
                                   _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
+    L.sd_lightspec_update.restype = _I
+    L.sd_lightspec_update.argtypes = [_P, _I, _I, _P, _P, _P, ctypes.c_double, _P, _P]
+    L.sd_lightspec_plan_workspace_size.restype = _SZ
+    L.sd_lightspec_plan_workspace_size.argtypes = [_I, _I]
+    L.sd_lightspec_plan.restype = _I
+    L.sd_lightspec_plan.argtypes = [_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _SZ]
     L.sd_stream_read_sink_words.restype = ctypes.c_longlong
     L.sd_stream_read_sink_words.argtypes = [ctypes.c_longlong]
     L.sd_stream_read.restype = _I
@@ -249,3 +257,43 @@ def sd_stream_read(src, sink=None, stream=None):
     _check("sd_stream_read", lib().sd_stream_read(_stream(stream), _ptr(src, name="src"), nbytes,
                                                   _ptr(sink, torch.int32, "sink")))
     return sink
+
+
+def sd_lightspec_update(alpha, ell, status, lam, ema, count, stream=None):
+    """Fold one verify step's acceptance probabilities alpha [R][gmax] fp32
+    into the per-position EMA state ema [gmax] fp64 / count [gmax] int64
+    (updated in place on the device)."""
+    R, gmax = alpha.shape
+    _check("sd_lightspec_update", lib().sd_lightspec_update(
+        _stream(stream), R, gmax, _ptr(alpha, torch.float32, "alpha"), _ptr(ell, torch.int32, "ell"),
+        _ptr(status, torch.int32, "status"), float(lam), _ptr(ema, torch.float64, "ema"),
+        _ptr(count, torch.int64, "count")))
+
+
+def sd_lightspec_plan(ema, count, d_prev, sps, draft_cost, out=None, workspace=None, stream=None):
+    """Both planning stages.  d_prev [R] int32 (the previous round's draft
+    lengths).  Returns a dict of device tensors: conf (planning confidences),
+    ell, batch, n_sel, theta (stage 1), d_next, b_next, phi (stage 2)."""
+    gmax = ema.shape[0]
+    R = d_prev.shape[0]
+    dev = ema.device
+    o = out or {}
+    conf = o.get("conf", torch.empty(gmax, dtype=torch.float32, device=dev))
+    ell = o.get("ell", torch.empty(R, dtype=torch.int32, device=dev))
+    batch = o.get("batch", torch.empty(1, dtype=torch.int32, device=dev))
+    n_sel = o.get("n_sel", torch.empty(1, dtype=torch.int32, device=dev))
+    theta = o.get("theta", torch.empty(1, dtype=torch.float64, device=dev))
+    d_next = o.get("d_next", torch.empty(1, dtype=torch.int32, device=dev))
+    b_next = o.get("b_next", torch.empty(1, dtype=torch.int32, device=dev))
+    phi = o.get("phi", torch.empty(gmax, dtype=torch.float64, device=dev))
+    wsz = lib().sd_lightspec_plan_workspace_size(R, gmax)
+    ws = workspace if workspace is not None else _workspace(wsz, dev)
+    _check("sd_lightspec_plan", lib().sd_lightspec_plan(
+        _stream(stream), R, gmax, _ptr(ema, torch.float64, "ema"), _ptr(count, torch.int64, "count"),
+        _ptr(d_prev, torch.int32, "d_prev"), _ptr(sps, torch.float32, "sps"), sps.numel(),
+        _ptr(draft_cost, torch.float32, "draft_cost"), _ptr(conf, torch.float32),
+        _ptr(ell, torch.int32), _ptr(batch, torch.int32), _ptr(n_sel, torch.int32),
+        _ptr(theta, torch.float64), _ptr(d_next, torch.int32), _ptr(b_next, torch.int32),
+        _ptr(phi, torch.float64), ws.data_ptr(), ws.numel()))
+    return dict(conf=conf, ell=ell, batch=batch, n_sel=n_sel, theta=theta, d_next=d_next,
+                b_next=b_next, phi=phi)

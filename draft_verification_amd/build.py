@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdv.so")
-SOURCES = ["abi.hip", "schedule.hip", "row_partials.hip", "verify.hip", "markov.hip", "probe.hip"]
+SOURCES = ["abi.hip", "schedule.hip", "row_partials.hip", "verify.hip", "markov.hip", "lightspec.hip",
+           "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -247,6 +247,57 @@ int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
                     void* workspace, size_t workspace_bytes);
 
 /*
+ * Training-free two-stage budget planner [LS: two optimisation stages, EMA
+ * runtime statistics with interpolation across draft lengths, runtime cost
+ * tables].  Readings: the statistics are one EMA per draft position of the
+ * acceptance probability alpha_j = sum_v min(p_j, q_j) (sd_verify's
+ * accept_prob, [DS 2.1]'s confidence label); the planner feeds them to the
+ * prefix scheduler as every request's confidences.
+ *
+ * sd_lightspec_update - fold one verify step into the table: for position
+ * j = 1..gamma_max, over the requests r (in order) with ell[r] >= j whose
+ * status has neither NONFINITE nor ZERO_Z, mean_j = (sum alpha[r][j-1]) / n_j
+ * in fp64; if count[j-1] == 0 then ema[j-1] = mean_j, else
+ * ema[j-1] = (1 - lambda) * ema[j-1] + lambda * mean_j (unfused fp64);
+ * count[j-1] += n_j.  Positions with n_j = 0 are left alone.
+ *   alpha [R][gamma_max] fp32, ell [R], status [R] int32 (device);
+ *   lambda in [0, 1];  ema [gamma_max] fp64 and count [gamma_max] int64 are
+ *   caller-owned device state (initialise count to 0 and ema to a prior).
+ *
+ * sd_lightspec_plan - both stages on the device.
+ *   conf_hat[j-1]: ema[j-1] where count > 0; elsewhere linear interpolation
+ *     between the nearest positions with count > 0, held constant past the
+ *     first / last one; if none has count > 0, ema as given; clamped to [0, 1]
+ *     and rounded to fp32.
+ *   stage 1 (verify budget): sd_schedule in GLOBAL_ARGMAX mode on
+ *     conf[r][j] = conf_hat[j] with gamma_r = d_prev (the previous round's draft
+ *     lengths; NULL means gamma_max): ell, batch, n_sel, theta as there.
+ *   stage 2 (draft budget): for d = 1..gamma_max with every request drafting
+ *     d tokens, n*(d) = smallest n in [0, R d] maximising Theta_n and
+ *       phi[d-1] = (R + tau_{n*}) / (draft_cost[d-1] + 1 / sps[R + n* - 1])
+ *     (fp64, unfused): expected emitted tokens per unit time when drafting
+ *     d tokens costs draft_cost[d-1] and a verify pass at batch B runs
+ *     sps[B-1] times per unit time.  d_next = smallest d maximising phi,
+ *     b_next = R + n*(d_next).
+ *   sps [sps_len] fp32, sps_len >= R * (1 + gamma_max); draft_cost
+ *   [gamma_max] fp32; conf_hat [gamma_max] fp32 out or NULL; ell [R], batch,
+ *   n_sel, theta as in sd_schedule; d_next, b_next [1] int32 out; phi
+ *   [gamma_max] fp64 out or NULL; workspace at least
+ *   sd_lightspec_plan_workspace_size(R, gamma_max) bytes, 256-byte aligned.
+ *   R * gamma_max <= SD_MAX_SCHED_SLOTS.  Four launches, nothing read back.
+ */
+int sd_lightspec_update(hipStream_t stream, int R, int gamma_max, const float* alpha,
+                        const int32_t* ell, const int32_t* status, double lambda,
+                        double* ema, int64_t* count);
+size_t sd_lightspec_plan_workspace_size(int R, int gamma_max);
+int sd_lightspec_plan(hipStream_t stream, int R, int gamma_max, const double* ema,
+                      const int64_t* count, const int32_t* d_prev, const float* sps,
+                      int sps_len, const float* draft_cost, float* conf_hat,
+                      int32_t* ell, int32_t* batch, int32_t* n_sel, double* theta,
+                      int32_t* d_next, int32_t* b_next, double* phi,
+                      void* workspace, size_t workspace_bytes);
+
+/*
  * Measurement aid, not part of the method.
  *
  * sd_stream_read - stream `bytes` bytes of device memory at `src` with the

@@ -118,3 +118,26 @@ def test_stream_read_host_validation():
     assert L.sd_stream_read(None, None, 32, p) == _lib.SD_EINVAL     # no source
     assert L.sd_stream_read(None, ctypes.c_void_p(8), 32, p) == _lib.SD_EINVAL   # misaligned
     assert L.sd_stream_read(None, p, 0, None) == _lib.SD_OK          # nothing to read
+
+
+def test_lightspec_host_validation():
+    L = sdv.lib()
+    p = ctypes.c_void_p(256)
+    for lam in (float("nan"), -0.1, 1.5):
+        assert L.sd_lightspec_update(None, 4, 4, p, p, p, lam, p, p) == _lib.SD_EINVAL
+    assert L.sd_lightspec_update(None, 4, 256, p, p, p, 0.1, p, p) == _lib.SD_EUNSUPPORTED
+    assert L.sd_lightspec_update(None, 4, 4, None, p, p, 0.1, p, p) == _lib.SD_EINVAL
+    assert L.sd_lightspec_update(None, 0, 4, None, None, None, 0.1, None, None) == _lib.SD_OK
+    ws = L.sd_lightspec_plan_workspace_size(4, 4)
+    assert ws >= L.sd_schedule_workspace_size(4, 4)
+
+    def plan(R=4, g=4, sps_len=20, wsb=ws, nulls=()):
+        P = lambda name: None if name in nulls else p
+        return L.sd_lightspec_plan(None, R, g, P("ema"), P("cnt"), None, P("sps"), sps_len, P("cost"),
+                                   None, P("ell"), None, None, None, P("dn"), P("bn"), None, p, wsb)
+
+    assert plan(sps_len=19) == _lib.SD_ERANGE
+    assert plan(wsb=ws - 1) == _lib.SD_ERANGE
+    assert plan(R=2048, g=16, sps_len=40000) == _lib.SD_EUNSUPPORTED
+    assert plan(nulls=("cost",)) == _lib.SD_EINVAL
+    assert plan(nulls=("dn",)) == _lib.SD_EINVAL
