@@ -15,7 +15,7 @@ Sources (cited by page title and section):
   * "DSpark: Confidence-Scheduled Speculative Decoding with Semi-Autoregressive
     Generation" (paper summary page): section "2.1 confidence head",
     "2.2 hardware-aware prefix scheduler", Figure 1, "challenge 2: async
-    scheduling and ZOS".
+    scheduling and ZOS", "innovation one" (Markov and RNN sequential heads).
   * speculative-decoding history page: "1.1 mechanism" (draft, parallel verify,
     rejection sampling, losslessness), DSpark "move one" (Markov head) and
     "move two / move three" (survival products, greedy scheduler).
@@ -27,4 +27,4 @@ Sources (cited by page title and section):
 Parity status per function is stated in each module header.
 """
 
-from . import rng, schedule, verify, markov, bf16, lightspec  # noqa: F401
+from . import rng, schedule, verify, markov, bf16, lightspec, rnn  # noqa: F401

@@ -62,6 +62,21 @@ def markov_step(U_k, A_k, C_k, x_prev, h_k, E, w, T, seed, req_ids, pos):
 
     bias_rows = np.where(valid[:, None], np.asarray(A_k, np.float64)[xs], 0.0)
     y = U_k + bias_rows @ np.asarray(C_k, np.float64)
+    L, tokens, conf, status, dists = draw_position(y, x_prev, h_k, E, w, T, seed, req_ids, pos,
+                                                   status)
+    return y, L, tokens, conf, status, dists
+
+
+def draw_position(y, x_prev, h_k, E, w, T, seed, req_ids, pos, status):
+    """Shared by the sequential heads: round the exact logits y[n][V] to bf16,
+    the confidence from h_k and E[x_prev], and the inverse-CDF draw.
+    Returns (L, tokens, conf, status, dists)."""
+    n, V = y.shape
+    H = h_k.shape[1]
+    x_prev = np.asarray(x_prev, np.int64)
+    valid = (x_prev >= 0) & (x_prev < V)
+    xs = np.where(valid, x_prev, 0)
+    status = np.asarray(status, np.int32).copy()
     L = round_to_bf16(y)
 
     emb = np.where(valid[:, None], np.asarray(E, np.float64)[xs], 0.0)
@@ -84,7 +99,7 @@ def markov_step(U_k, A_k, C_k, x_prev, h_k, E, w, T, seed, req_ids, pos):
         wts = np.exp(x - m)
         u = uniform(seed, int(req_ids[i]), int(pos[i]), DRAW_DRAFT)
         tokens[i], dists[i] = inverse_cdf(wts, u)
-    return y, L, tokens, conf, status, dists
+    return L, tokens, conf, status, dists
 
 
 def markov_draft(U, A, C, x0, h, E, w, T, seed, pos0=None):
