@@ -202,6 +202,40 @@ def bench_planner(sdv, torch, inp, vo, ell):
             "plan_us": round(graph_time_us(torch, pln), 2), "launches": 5}
 
 
+def bench_rnn(sdv, torch, steps):
+    """The RNN drafting head at R=128, gamma=16, V=129280, d=128."""
+    from workloads import rnn_config
+    inp = rnn_config(device="cuda")
+    R, g, V, d = inp["R"], inp["gamma"], inp["V"], inp["d"]
+    dev = "cuda"
+    out = dict(tokens=torch.empty((R, g), dtype=torch.int32, device=dev),
+               q_logits=torch.empty((R, g, V), dtype=torch.bfloat16, device=dev),
+               conf=torch.empty((R, g), dtype=torch.float32, device=dev),
+               status=torch.empty(R, dtype=torch.int32, device=dev))
+    ws = torch.empty(max(sdv.sd_rnn_draft_workspace_size(R, g, V, d), 256), dtype=torch.uint8, device=dev)
+    call = lambda: sdv.sd_rnn_draft(inp["U"], inp["W"], inp["Es"], inp["Ct"], inp["x0"], inp["h"],
+                                    inp["E"], inp["w"], 1.0, inp["seed"], workspace=ws, out=out)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    n = max(3, min(steps, 20))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    hbm = (2 * g * V * d + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # C per step + U + L + h
+    flops = 2.0 * R * (2 * d) * V * g                                      # two bf16 terms of the state
+    return {"workload": f"R={R}, gamma={g}, V={V}, d={d}, H=4096, bf16",
+            "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
+            "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
+            "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
+            "launches": 2 * g + 2}
+
+
 def bench_markov(sdv, torch, steps, hip):
     from workloads import markov_config
     inp = markov_config(device="cuda")
@@ -233,7 +267,7 @@ def bench_markov(sdv, torch, steps, hip):
             "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
             "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
             "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
-            "launches": 2 * g + 1}
+            "launches": 2 * g + 2}
 
 
 def main():
@@ -395,6 +429,8 @@ def main():
     if not args.no_markov:
         print("markov head", file=sys.stderr, flush=True)
         result["markov_draft"] = bench_markov(sdv, torch, K, hip)
+        print("rnn head", file=sys.stderr, flush=True)
+        result["rnn_draft"] = bench_rnn(sdv, torch, K)
     if not args.no_cpu_baseline:
         print("cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(sets[0], ell_full)

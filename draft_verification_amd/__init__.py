@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     sd_verify_workspace_size,
     sd_markov_draft,
     sd_markov_draft_workspace_size,
+    sd_rnn_draft,
+    sd_rnn_draft_workspace_size,
     sd_stream_read,
     sd_lightspec_update,
     sd_lightspec_plan,

@@ -38,6 +38,7 @@ EXPORTS = (
     "sd_abi_version", "sd_status_string", "sd_schedule_workspace_size", "sd_schedule",
     "sd_verify_workspace_size",
     "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
+    "sd_rnn_draft_workspace_size", "sd_rnn_draft",
     "sd_lightspec_update", "sd_lightspec_plan_workspace_size", "sd_lightspec_plan",
     "sd_stream_read_sink_words", "sd_stream_read",
 )
@@ -82,6 +83,11 @@ def lib():
     L.sd_markov_draft.restype = _I
     L.sd_markov_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P,
                                   _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
+    L.sd_rnn_draft_workspace_size.restype = _SZ
+    L.sd_rnn_draft_workspace_size.argtypes = [_I, _I, _I, _I]
+    L.sd_rnn_draft.restype = _I
+    L.sd_rnn_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P, _P, _P,
+                               _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
     L.sd_lightspec_update.restype = _I
     L.sd_lightspec_update.argtypes = [_P, _I, _I, _P, _P, _P, ctypes.c_double, _P, _P]
     L.sd_lightspec_plan_workspace_size.restype = _SZ
@@ -241,6 +247,37 @@ def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, w
         _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf), _ptr(conf, torch.float32),
         _ptr(status, torch.int32), ws.data_ptr(), ws.numel())
     _check("sd_markov_draft", code)
+    return dict(tokens=tokens, q_logits=ql, conf=conf, status=status)
+
+
+def sd_rnn_draft_workspace_size(R, gamma, V, d):
+    return lib().sd_rnn_draft_workspace_size(R, gamma, V, d)
+
+
+def sd_rnn_draft(U, W, Es, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, workspace=None,
+                 out=None, stream=None):
+    """Run the RNN drafting head.  Returns a dict of device tensors:
+    tokens [R][gamma], q_logits [R][gamma][V] bf16, conf [R][gamma], status [R]."""
+    R, gamma, V = U.shape
+    d = W.shape[0]
+    H = h.shape[2]
+    rank_e = E.shape[1]
+    dev = U.device
+    bf = torch.bfloat16
+    o = out or {}
+    tokens = o.get("tokens", torch.empty((R, gamma), dtype=torch.int32, device=dev))
+    ql = o.get("q_logits", torch.empty((R, gamma, V), dtype=bf, device=dev))
+    conf = o.get("conf", torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
+    ws = workspace if workspace is not None else _workspace(sd_rnn_draft_workspace_size(R, gamma, V, d),
+                                                            dev)
+    code = lib().sd_rnn_draft(
+        _stream(stream), R, gamma, V, d, float(temperature), int(seed) & (2**64 - 1),
+        _ptr(pos0, torch.int64, "pos0"), _ptr(U, bf, "U"), _ptr(W, bf, "W"), _ptr(Es, bf, "Es"),
+        _ptr(Ct, bf, "Ct"), _ptr(x0, torch.int32, "x0"), _ptr(h, bf, "h"), H, _ptr(E, bf, "E"), rank_e,
+        _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf), _ptr(conf, torch.float32),
+        _ptr(status, torch.int32), ws.data_ptr(), ws.numel())
+    _check("sd_rnn_draft", code)
     return dict(tokens=tokens, q_logits=ql, conf=conf, status=status)
 
 

@@ -105,12 +105,17 @@ __global__ __launch_bounds__(64) void k_gather_a(int R, int V, int rank, const u
 }
 
 // ---------------------------------------------------------------------------
-// G tile = Ag[m0..m0+127] (128 x rank) . Ct_k[n0..n0+127]^T (rank x 128)
-// with v_mfma_f32_16x16x32_bf16: wave w owns columns [32w, 32w+32) of the tile,
-// all 128 rows: 8 row blocks x 2 column blocks of 16 x 16 accumulators.
-__global__ __launch_bounds__(kThreads) void k_markov_bias(
-    int R, int gamma, int k, int V, int rank, float c, const uint16_t* __restrict__ U,
-    const uint16_t* __restrict__ Ct, const uint16_t* __restrict__ Ag,
+// G tile = A rows (128 x kdim) . Ct_k[n0..n0+127]^T (kdim x 128) with
+// v_mfma_f32_16x16x32_bf16: wave w owns columns [32w, 32w+32) of the tile, all
+// 128 rows: 8 row blocks x 2 column blocks of 16 x 16 accumulators.
+// NSPLIT = 1: Ag[r] holds A_k[x_{k-1}] (the Markov head).  NSPLIT = 2: Ag[r]
+// holds the RNN state as two bf16 terms, hi = bf16(s) then lo = bf16(s - hi),
+// and both are multiplied by the same C fragments, so the product carries the
+// fp32 state to within 2^-17 of each element.
+template <int NSPLIT>
+__global__ __launch_bounds__(kThreads, 2) void k_markov_bias(
+    int R, int gamma, int k, int V, int kdim, float c, const uint16_t* __restrict__ U,
+    const uint16_t* __restrict__ Ct, size_t ct_stride, const uint16_t* __restrict__ Ag,
     uint16_t* __restrict__ q_logits, float2* __restrict__ partial, int n_tiles) {
   // LDS: the A rows during the GEMM, then the fp32 output tile.
   constexpr int kAbytes = kTileM * (kMaxRank + kApad) * 2;
@@ -125,13 +130,14 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
   const int tile = blockIdx.x;
   const int n0 = tile * kTileN;
   const int m0 = blockIdx.y * kTileM;
-  const int lda = rank + kApad;
-  const int ksteps = rank / 32;
-  const uint16_t* Ck = Ct + (size_t)(k - 1) * V * rank;
+  const int arow = NSPLIT * kdim;  // bf16 per A row
+  const int lda = arow + kApad;
+  const int kb = kdim / 32;        // K steps of the C fragments
+  const uint16_t* Ck = Ct + (size_t)(k - 1) * ct_stride;
 
   // Every HBM read of the workgroup is issued before the first wait: the A
   // rows (needed first), the B fragments, then the U tile for the epilogue.
-  const int vec_per_row = rank / 8;
+  const int vec_per_row = arow / 8;
   const int total = kTileM * vec_per_row;
   uint4 gat[kAPerThread];
 #pragma unroll
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
     const int idx = tid + i * kThreads;
     const int row = idx / vec_per_row;
     gat[i] = (idx < total && m0 + row < R)
-                 ? *(const uint4*)(Ag + (size_t)(m0 + row) * rank + (idx % vec_per_row) * 8)
+                 ? *(const uint4*)(Ag + (size_t)(m0 + row) * arow + (idx % vec_per_row) * 8)
                  : make_uint4(0, 0, 0, 0);
   }
   // B fragments: lane l holds column (l % 16) of its 16-column block,
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
 #pragma unroll
     for (int ks = 0; ks < kMaxRank / 32; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (ks < ksteps && col < V) v = sdv::ld_nt(Ck + (size_t)col * rank + ks * 32 + (lane >> 4) * 8);
+      if (ks < kb && col < V) v = sdv::ld_nt(Ck + (size_t)col * kdim + ks * 32 + (lane >> 4) * 8);
       bfrag[nb][ks] = v;
     }
   }
@@ -180,16 +186,19 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
 
 #pragma unroll
   for (int ks = 0; ks < kMaxRank / 32; ++ks) {
-    if (ks < ksteps) {
+    if (ks < kb) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const uint4 av =
-            *(const uint4*)(sA + (mb * 16 + (lane & 15)) * lda + ks * 32 + (lane >> 4) * 8);
-        const bf16x8 a = as_bf16x8(av);
+      for (int sp = 0; sp < NSPLIT; ++sp) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bfrag[nb][ks]), acc[mb][nb], 0, 0, 0);
+        for (int mb = 0; mb < 8; ++mb) {
+          const uint4 av = *(const uint4*)(sA + (mb * 16 + (lane & 15)) * lda + (sp * kb + ks) * 32 +
+                                           (lane >> 4) * 8);
+          const bf16x8 a = as_bf16x8(av);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bfrag[nb][ks]),
+                                                                  acc[mb][nb], 0, 0, 0);
+        }
       }
     }
   }
@@ -243,14 +252,61 @@ __global__ __launch_bounds__(kThreads) void k_markov_bias(
 }
 
 // ---------------------------------------------------------------------------
+// The rows the next step's bias multiplies, once x_k is known (every thread
+// calls).  Markov: Ag[r] = A_{k+1}[x_k], zeros for an invalid token.  RNN:
+// s_{k+1} = tanh(W s_k + E_s[x_k]) in fp32 (no embedding term for an invalid
+// token), kept in state[r] and written to Ag[r] as its two bf16 terms.
+struct NextRows {
+  int rank;                 // Markov: A row length; RNN: state size d
+  const uint16_t* A;        // Markov: A [gamma][V][rank]
+  const uint16_t* W;        // RNN: W [d][d]
+  const uint16_t* Es;       // RNN: E_s [V][d]
+  float* state;             // RNN: [R][d]
+  uint16_t* Ag;             // [R][rank] (Markov) or [R][2d] (RNN)
+};
+
+template <bool RNN>
+__device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, float* s_s) {
+  const int tid = threadIdx.x;
+  const bool valid = tok >= 0 && tok < V;
+  if constexpr (!RNN) {
+    const uint16_t* Anext = nr.A + (size_t)k * V * nr.rank;
+    for (int v = tid; v < nr.rank / 8; v += kThreads)
+      ((uint4*)(nr.Ag + (size_t)r * nr.rank))[v] =
+          valid ? ((const uint4*)(Anext + (size_t)tok * nr.rank))[v] : make_uint4(0, 0, 0, 0);
+  } else {
+    const int d = nr.rank;
+    for (int i = tid; i < d; i += kThreads) s_s[i] = nr.state[(size_t)r * d + i];
+    __syncthreads();
+    for (int o = tid; o < d; o += kThreads) {
+      const uint16_t* wr = nr.W + (size_t)o * d;
+      float acc = 0.0f;
+      for (int i = 0; i < d; i += 8) {
+        const uint4 q = *(const uint4*)(wr + i);
+        acc += sdv::bf16lo(q.x) * s_s[i] + sdv::bf16hi(q.x) * s_s[i + 1] +
+               sdv::bf16lo(q.y) * s_s[i + 2] + sdv::bf16hi(q.y) * s_s[i + 3] +
+               sdv::bf16lo(q.z) * s_s[i + 4] + sdv::bf16hi(q.z) * s_s[i + 5] +
+               sdv::bf16lo(q.w) * s_s[i + 6] + sdv::bf16hi(q.w) * s_s[i + 7];
+      }
+      if (valid) acc += sdv::bf16_to_f32(nr.Es[(size_t)tok * d + o]);
+      const float sn = tanhf(acc);
+      nr.state[(size_t)r * d + o] = sn;
+      const uint16_t hi = sdv::f32_to_bf16_rne(sn);
+      nr.Ag[(size_t)r * 2 * d + o] = hi;
+      nr.Ag[(size_t)r * 2 * d + d + o] = sdv::f32_to_bf16_rne(sn - sdv::bf16_to_f32(hi));
+    }
+  }
+}
+
+template <bool RNN>
 __global__ __launch_bounds__(kThreads) void k_markov_select(
     int gamma, int k, int V, int H, int rank_e, float c, uint64_t seed,
     const int64_t* __restrict__ pos0, const int32_t* __restrict__ x0,
     const uint16_t* __restrict__ E, const float* __restrict__ w,
     const float* __restrict__ hdot, const float2* __restrict__ partial, int n_tiles,
-    const uint16_t* __restrict__ q_logits, int rank, const uint16_t* __restrict__ A,
-    uint16_t* __restrict__ Ag, int32_t* __restrict__ tokens, float* __restrict__ conf,
-    int32_t* __restrict__ status) {
+    const uint16_t* __restrict__ q_logits, NextRows nr, int32_t* __restrict__ tokens,
+    float* __restrict__ conf, int32_t* __restrict__ status) {
+  __shared__ float s_s[kMaxRank];
   __shared__ float s_red[kThreads / 64];
   __shared__ double s_redd[kThreads / 64];
   __shared__ int s_tile;
@@ -316,9 +372,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       tokens[(size_t)r * gamma + (k - 1)] = -1;
       status[r] = st | bad;
     }
-    if (k < gamma)  // no anchor for the next step: no Markov bias
-      for (int v = tid; v < rank / 8; v += kThreads)
-        ((uint4*)(Ag + (size_t)r * rank))[v] = make_uint4(0, 0, 0, 0);
+    if (k < gamma) next_rows<RNN>(nr, r, k, V, -1, s_s);  // no valid token to carry forward
     return;
   }
 
@@ -398,20 +452,69 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     tokens[(size_t)r * gamma + (k - 1)] = tok;
     status[r] = st;
   }
-  if (k < gamma) {  // the next step's Markov rows: A_{k+1}[x_k]
-    const bool valid = tok >= 0 && tok < V;
-    const uint16_t* Anext = A + (size_t)k * V * rank;
-    for (int v = tid; v < rank / 8; v += kThreads)
-      ((uint4*)(Ag + (size_t)r * rank))[v] =
-          valid ? ((const uint4*)(Anext + (size_t)tok * rank))[v] : make_uint4(0, 0, 0, 0);
+  if (k < gamma) next_rows<RNN>(nr, r, k, V, tok, s_s);
+}
+
+// s_1 = tanh(W s_0 + E_s[x_0]) = tanh(E_s[x_0]) (s_0 = 0; no embedding term for
+// an anchor outside [0, V)), kept in state[r] and written to Ag[r] split.
+__global__ __launch_bounds__(kThreads) void k_rnn_init(int R, int V, int d, const uint16_t* __restrict__ Es,
+                                                       const int32_t* __restrict__ x0,
+                                                       float* __restrict__ state,
+                                                       uint16_t* __restrict__ Ag) {
+  const int r = blockIdx.x;
+  const int x = x0[r];
+  const bool valid = x >= 0 && x < V;
+  for (int o = threadIdx.x; o < d; o += kThreads) {
+    const float sn = tanhf(valid ? sdv::bf16_to_f32(Es[(size_t)x * d + o]) : 0.0f);
+    state[(size_t)r * d + o] = sn;
+    const uint16_t hi = sdv::f32_to_bf16_rne(sn);
+    Ag[(size_t)r * 2 * d + o] = hi;
+    Ag[(size_t)r * 2 * d + d + o] = sdv::f32_to_bf16_rne(sn - sdv::bf16_to_f32(hi));
   }
 }
 
-size_t markov_ws_bytes(int R, int gamma, int V, int rank) {
+// Workspace: hdot [R][gamma] fp32, tile partials [R][n_tiles] float2, the next
+// step's A rows [R][arow] bf16, RNN state [R][d] fp32 (d = 0 for Markov).
+size_t head_ws_bytes(int R, int gamma, int V, int arow, int d) {
   const size_t n_tiles = ((size_t)V + kTileN - 1) / kTileN;
   return sdv_align256((size_t)R * gamma * sizeof(float)) +
          sdv_align256((size_t)R * n_tiles * sizeof(float2)) +
-         sdv_align256((size_t)R * rank * sizeof(uint16_t));
+         sdv_align256((size_t)R * arow * sizeof(uint16_t)) +
+         sdv_align256((size_t)R * d * sizeof(float));
+}
+size_t markov_ws_bytes(int R, int gamma, int V, int rank) { return head_ws_bytes(R, gamma, V, rank, 0); }
+size_t rnn_ws_bytes(int R, int gamma, int V, int d) { return head_ws_bytes(R, gamma, V, 2 * d, d); }
+
+// Checks shared by both heads (everything but the head's own tables).
+int check_head_args(int R, int gamma, int V, int H, int rank_e, float temperature) {
+  if (R < 0 || gamma < 0 || V < 8 || (V % 8) != 0 || H < 0 || (H % 8) != 0 || rank_e < 0 ||
+      (rank_e % 8) != 0)
+    return SD_EINVAL;
+  if (gamma > SD_MAX_GAMMA || V > SD_MAX_VOCAB) return SD_EUNSUPPORTED;
+  if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf())) return SD_EINVAL;
+  return SD_OK;
+}
+
+// The sequential loop shared by both heads: per step the bias GEMM + epilogue,
+// then the select kernel (which also prepares the next step's rows).
+template <int NSPLIT>
+int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_stride, float c,
+             uint64_t seed, const int64_t* pos0, const uint16_t* U, const uint16_t* Ct,
+             const int32_t* x0, int H, const uint16_t* E, int rank_e, const float* w,
+             const float* hdot, float2* partial, const NextRows& nr, int32_t* tokens,
+             uint16_t* q_logits, float* conf, int32_t* status) {
+  const int n_tiles = (V + kTileN - 1) / kTileN;
+  const dim3 grid_bias(n_tiles, (R + kTileM - 1) / kTileM);
+  for (int k = 1; k <= gamma; ++k) {
+    SDV_TRY_LAUNCH(sdv::launch(k_markov_bias<NSPLIT>, grid_bias, dim3(kThreads), 0, stream, R, gamma,
+                               k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag, q_logits,
+                               partial, n_tiles));
+    SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT == 2>, dim3(R), dim3(kThreads), 0, stream, gamma,
+                               k, V, H, rank_e, c, seed, pos0, x0, E, w, hdot,
+                               (const float2*)partial, n_tiles, (const uint16_t*)q_logits, nr, tokens,
+                               conf, status));
+  }
+  return SD_OK;
 }
 
 }  // namespace
@@ -428,46 +531,79 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
                                int rank_e, const float* w, int32_t* tokens, uint16_t* q_logits,
                                float* conf, int32_t* status, void* workspace,
                                size_t workspace_bytes) {
-  if (R < 0 || gamma < 0 || V < 8 || (V % 8) != 0 || H < 0 || (H % 8) != 0 || rank_e < 0 ||
-      (rank_e % 8) != 0)
-    return SD_EINVAL;
+  const int rc = check_head_args(R, gamma, V, H, rank_e, temperature);
+  if (rc != SD_OK) return rc;
   if (rank < 32 || (rank % 32) != 0) return SD_EINVAL;
-  if (rank > kMaxRank || gamma > SD_MAX_GAMMA || V > SD_MAX_VOCAB) return SD_EUNSUPPORTED;
-  if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf())) return SD_EINVAL;
-  const int n_tiles = (V + kTileN - 1) / kTileN;
+  if (rank > kMaxRank) return SD_EUNSUPPORTED;
   if (R == 0 || gamma == 0) return SD_OK;
   if (!U || !A || !Ct || !x0 || !w || !tokens || !q_logits || !conf || !status) return SD_EINVAL;
   if ((H > 0 && !h) || (rank_e > 0 && !E)) return SD_EINVAL;
+  if (H == 0) return SD_EINVAL;  // the confidence head needs a hidden state
   if (!workspace || workspace_bytes < markov_ws_bytes(R, gamma, V, rank)) return SD_ERANGE;
   if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
   if ((((uintptr_t)U | (uintptr_t)A | (uintptr_t)Ct | (uintptr_t)q_logits | (uintptr_t)h |
         (uintptr_t)w) & 15) != 0)
     return SD_EINVAL;
 
-  const float c = sdv::kLog2e / temperature;
+  const int n_tiles = (V + kTileN - 1) / kTileN;
+  char* p = (char*)workspace;
+  float* hdot = (float*)p;
+  p += sdv_align256((size_t)R * gamma * sizeof(float));
+  float2* partial = (float2*)p;
+  p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
+  NextRows nr{rank, A, nullptr, nullptr, nullptr, (uint16_t*)p};
+
+  const int rows = R * gamma;
+  SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
+                             rows, hdot));
+  SDV_TRY_LAUNCH(sdv::launch(k_gather_a, dim3(R), dim3(64), 0, stream, R, V, rank, A, x0, nr.Ag));
+  return run_head<1>(stream, R, gamma, V, rank, (size_t)V * rank, sdv::kLog2e / temperature, seed,
+                     pos0, U, Ct, x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf,
+                     status);
+}
+
+extern "C" size_t sd_rnn_draft_workspace_size(int R, int gamma, int V, int d) {
+  if (R < 0 || gamma < 0 || V <= 0 || d < 0) return 0;
+  return rnn_ws_bytes(R, gamma, V, d);
+}
+
+extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, float temperature,
+                            uint64_t seed, const int64_t* pos0, const uint16_t* U,
+                            const uint16_t* W, const uint16_t* Es, const uint16_t* Ct,
+                            const int32_t* x0, const uint16_t* h, int H, const uint16_t* E,
+                            int rank_e, const float* w, int32_t* tokens, uint16_t* q_logits,
+                            float* conf, int32_t* status, void* workspace,
+                            size_t workspace_bytes) {
+  const int rc = check_head_args(R, gamma, V, H, rank_e, temperature);
+  if (rc != SD_OK) return rc;
+  if (d < 32 || (d % 32) != 0) return SD_EINVAL;
+  if (2 * d > kMaxRank) return SD_EUNSUPPORTED;
+  if (R == 0 || gamma == 0) return SD_OK;
+  if (!U || !W || !Es || !Ct || !x0 || !w || !tokens || !q_logits || !conf || !status)
+    return SD_EINVAL;
+  if ((H > 0 && !h) || (rank_e > 0 && !E)) return SD_EINVAL;
+  if (H == 0) return SD_EINVAL;  // the confidence head needs a hidden state
+  if (!workspace || workspace_bytes < rnn_ws_bytes(R, gamma, V, d)) return SD_ERANGE;
+  if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
+  if ((((uintptr_t)U | (uintptr_t)W | (uintptr_t)Ct | (uintptr_t)q_logits | (uintptr_t)h |
+        (uintptr_t)w) & 15) != 0)
+    return SD_EINVAL;
+
+  const int n_tiles = (V + kTileN - 1) / kTileN;
   char* p = (char*)workspace;
   float* hdot = (float*)p;
   p += sdv_align256((size_t)R * gamma * sizeof(float));
   float2* partial = (float2*)p;
   p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
   uint16_t* Ag = (uint16_t*)p;
+  p += sdv_align256((size_t)R * 2 * d * sizeof(uint16_t));
+  NextRows nr{d, nullptr, W, Es, (float*)p, Ag};
 
   const int rows = R * gamma;
-  if (H > 0) {
-    SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H,
-                               w, rows, hdot));
-  } else {
-    return SD_EINVAL;  // the confidence head needs a hidden state
-  }
-  SDV_TRY_LAUNCH(sdv::launch(k_gather_a, dim3(R), dim3(64), 0, stream, R, V, rank, A, x0, Ag));
-  const dim3 grid_bias(n_tiles, (R + kTileM - 1) / kTileM);
-  for (int k = 1; k <= gamma; ++k) {
-    SDV_TRY_LAUNCH(sdv::launch(k_markov_bias, grid_bias, dim3(kThreads), 0, stream, R, gamma, k, V,
-                               rank, c, U, Ct, (const uint16_t*)Ag, q_logits, partial, n_tiles));
-    SDV_TRY_LAUNCH(sdv::launch(k_markov_select, dim3(R), dim3(kThreads), 0, stream, gamma, k, V, H,
-                               rank_e, c, seed, pos0, x0, E, w, (const float*)hdot,
-                               (const float2*)partial, n_tiles, (const uint16_t*)q_logits, rank, A,
-                               Ag, tokens, conf, status));
-  }
-  return SD_OK;
+  SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
+                             rows, hdot));
+  SDV_TRY_LAUNCH(sdv::launch(k_rnn_init, dim3(R), dim3(kThreads), 0, stream, R, V, d, Es, x0, nr.state,
+                             nr.Ag));
+  return run_head<2>(stream, R, gamma, V, d, 0, sdv::kLog2e / temperature, seed, pos0, U, Ct, x0, H,
+                     E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf, status);
 }

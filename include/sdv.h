@@ -247,6 +247,31 @@ int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
                     void* workspace, size_t workspace_bytes);
 
 /*
+ * sd_rnn_draft - the RNN form of the sequential head [DS innovation one]:
+ * instead of the previous token alone (Markov head) a recurrent state carries
+ * the drafted prefix.  Reading (the page gives no formula): an Elman cell,
+ *   s_k = tanh(W s_{k-1} + E_s[x_{k-1}]),  s_0 = 0,  (fp32)
+ *   L_k = bf16_rne( U[r][k-1] + s_k . C )     (C shared across positions)
+ * with x_k, conf and the degenerate cases exactly as sd_markov_draft (an
+ * anchor or token outside [0, V) contributes no embedding term).  The state
+ * enters the MFMA product as two bf16 terms (hi = bf16(s), lo = bf16(s - hi)),
+ * so each state element is carried to within 2^-17 of its fp32 value.
+ *   d % 32 == 0, 32 <= d <= 128; other limits as sd_markov_draft
+ *   W  [d][d] bf16 (row o: weights of output o);  Es [V][d] bf16
+ *   Ct [V][d] bf16: row n is column n of C
+ *   U, x0, h, H, E, rank_e, w, outputs as sd_markov_draft
+ *   workspace at least sd_rnn_draft_workspace_size(R, gamma, V, d) bytes,
+ *   256-byte aligned.
+ */
+size_t sd_rnn_draft_workspace_size(int R, int gamma, int V, int d);
+int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, float temperature,
+                 uint64_t seed, const int64_t* pos0, const uint16_t* U, const uint16_t* W,
+                 const uint16_t* Es, const uint16_t* Ct, const int32_t* x0, const uint16_t* h,
+                 int H, const uint16_t* E, int rank_e, const float* w, int32_t* tokens,
+                 uint16_t* q_logits, float* conf, int32_t* status, void* workspace,
+                 size_t workspace_bytes);
+
+/*
  * Training-free two-stage budget planner [LS: two optimisation stages, EMA
  * runtime statistics with interpolation across draft lengths, runtime cost
  * tables].  Readings: the statistics are one EMA per draft position of the

@@ -13,4 +13,6 @@ from .synth import (  # noqa: F401
     markov_config,
     markov_inputs,
     markov_targets,
+    rnn_config,
+    rnn_inputs,
 )

@@ -41,6 +41,9 @@ CONFIGS = {
 MARKOV = dict(R=128, gamma=16, V=129280, rank=256, H=4096, rank_e=256, sigma_u=2.0,
               sigma_f=0.02, sps=(256, 0.08, 64), seed_off=4)
 
+RNN = dict(R=128, gamma=16, V=129280, d=128, H=4096, rank_e=256, sigma_u=2.0, sigma_w=0.5,
+           sigma_e=1.0, sigma_c=0.05, sigma_f=0.02, seed_off=5)
+
 BASE_SEED = 20261202
 SAMPLE_SEED = 0xC0FFEE
 
@@ -196,6 +199,33 @@ def markov_config(device="cpu", **over):
     seed_off = cfg.pop("seed_off")
     cfg.update(over)
     return markov_inputs(seed=BASE_SEED + seed_off, device=device, **cfg)
+
+
+def rnn_inputs(R, gamma, V, d, H, rank_e, sigma_u=2.0, sigma_w=0.5, sigma_e=1.0, sigma_c=0.05,
+               sigma_f=0.02, seed=BASE_SEED + 5, device="cpu"):
+    """Inputs of the RNN drafting head: U [R][gamma][V], W [d][d] with entries
+    N(0, (sigma_w / sqrt(d))^2) (spectral radius about sigma_w), E_s [V][d]
+    N(0, sigma_e^2), Ct [V][d] N(0, sigma_c^2) (row v is column v of C), and
+    the confidence head's h, E, w as for the Markov head; all bf16 but w."""
+    g = _gen(device, seed)
+    bf = torch.bfloat16
+    U = _normal((R, gamma, V), sigma_u, g, device).to(bf)
+    W = _normal((d, d), sigma_w / math.sqrt(d), g, device).to(bf)
+    Es = _normal((V, d), sigma_e, g, device).to(bf)
+    Ct = _normal((V, d), sigma_c, g, device).to(bf)
+    h = _normal((R, gamma, H), 1.0, g, device).to(bf)
+    E = _normal((V, rank_e), sigma_f, g, device).to(bf)
+    w = _normal((H + rank_e,), sigma_f, g, device)
+    x0 = torch.randint(0, V, (R,), generator=g, device=device, dtype=torch.int32)
+    return dict(R=R, gamma=gamma, V=V, d=d, H=H, rank_e=rank_e, U=U, W=W, Es=Es, Ct=Ct, h=h, E=E,
+                w=w, x0=x0, temperature=1.0, seed=SAMPLE_SEED + 5, pos0=None)
+
+
+def rnn_config(device="cpu", **over):
+    cfg = dict(RNN)
+    seed_off = cfg.pop("seed_off")
+    cfg.update(over)
+    return rnn_inputs(seed=BASE_SEED + seed_off, device=device, **cfg)
 
 
 def markov_targets(q_logits, seed=BASE_SEED + 40, sigma=1.5, sigma_bonus=2.0):
