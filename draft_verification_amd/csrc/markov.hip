@@ -315,6 +315,16 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int xp = (k == 1) ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
+  // this thread's run of tile partials, requested before the confidence work
+  const float2* pp = partial + (size_t)r * n_tiles;
+  const int per = (n_tiles + kThreads - 1) / kThreads;
+  const int t0 = tid * per;
+  constexpr int kPre = 4;
+  float2 pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+    pre[i] = (i < per && t0 + i < n_tiles) ? pp[t0 + i] : make_float2(kNegInf, 0.0f);
+  auto part = [&](int i) { return i < kPre ? pre[i] : pp[t0 + i]; };
   const bool xvalid = xp >= 0 && xp < V;
   int st = (k == 1) ? 0 : status[r];
   if (!xvalid) st |= SD_ST_BAD_TOKEN;
@@ -334,11 +344,10 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   __syncthreads();
 
   // Combine the tile partials.  Thread t owns a contiguous run of tiles.
-  const float2* pp = partial + (size_t)r * n_tiles;
-  const int per = (n_tiles + kThreads - 1) / kThreads;
-  const int t0 = tid * per;
   float M = kNegInf;
-  for (int i = 0; i < per; ++i)
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) M = fmaxf(M, pre[i].x);
+  for (int i = kPre; i < per; ++i)
     if (t0 + i < n_tiles) M = fmaxf(M, pp[t0 + i].x);
   M = sdv::wave_max(M);
   if (lane == 0) s_red[wave] = M;
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   double own = 0.0;
   for (int i = 0; i < per; ++i) {
     if (t0 + i < n_tiles) {
-      const float2 q = pp[t0 + i];
+      const float2 q = part(i);
       if (q.y != 0.0f) own += (double)q.y * exp2((double)exp_ref(q.x, c) - (double)REF);
     }
   }
