@@ -9,18 +9,20 @@
 // "2.1 confidence head": c_k = sigmoid(w . [h_k ; E[x_{k-1}]]).
 //
 // Per step k (sequential over the block):
-//   k_markov_bias    the only dense contraction: G = A_k[x_{k-1}] . C_k as a
+//   k_head_bias      the only dense contraction: G = A_k[x_{k-1}] . C_k as a
 //                    bf16 MFMA GEMM (M = requests, N = vocabulary, K = rank),
 //                    fused with + U_k, bf16 rounding, the q_logits store and a
 //                    per-(row, 128-column tile) partial (max, sum 2^(L*c - ref));
-//                    the rows A_k[x_{k-1}] arrive pre-gathered, so every load
-//                    of a workgroup is issued before its first wait
+//                    loader waves stream C_k and U_k into LDS ahead of the
+//                    MFMA waves; the rows A_k[x_{k-1}] arrive pre-gathered
 //   k_markov_select  one workgroup per request: confidence of position k,
 //                    combine tile partials, locate the inverse-CDF tile,
 //                    rescan 128 logits, emit x_k, and gather A_{k+1}[x_k]
 //                    for the next step
 // plus, up front, one k_hidden_dot launch for w_h . h_k of every position and
 // one k_gather_a launch for A_1[x_0].
+#include <algorithm>
+
 #include "sdv_common.h"
 #include "sdv_host.h"
 
@@ -30,8 +32,6 @@ constexpr int kThreads = 256;
 constexpr int kTileN = 128;  // vocabulary columns per workgroup (4 waves x 32)
 constexpr int kTileM = 128;  // requests per workgroup
 constexpr int kMaxRank = 256;
-constexpr int kApad = 8;     // bf16 padding per LDS row of the gathered A rows
-constexpr int kGpad = 4;     // fp32 padding per LDS row of the output tile
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -105,149 +105,222 @@ __global__ __launch_bounds__(64) void k_gather_a(int R, int V, int rank, const u
 }
 
 // ---------------------------------------------------------------------------
-// G tile = A rows (128 x kdim) . Ct_k[n0..n0+127]^T (kdim x 128) with
-// v_mfma_f32_16x16x32_bf16: wave w owns columns [32w, 32w+32) of the tile, all
-// 128 rows: 8 row blocks x 2 column blocks of 16 x 16 accumulators.
-// NSPLIT = 1: Ag[r] holds A_k[x_{k-1}] (the Markov head).  NSPLIT = 2: Ag[r]
-// holds the RNN state as two bf16 terms, hi = bf16(s) then lo = bf16(s - hi),
-// and both are multiplied by the same C fragments, so the product carries the
-// fp32 state to within 2^-17 of each element.
+// The bias product G = Ag . C_k (M = requests, N = vocabulary, K = kdim) with
+// v_mfma_f32_16x16x32_bf16, fused with + U_k, the bf16 rounding, the q_logits
+// store and one partial (max, sum 2^(L*c - ref)) per (request, 128-column
+// tile).  NSPLIT = 1: Ag[r] holds A_k[x_{k-1}] (the Markov head).  NSPLIT = 2:
+// Ag[r] holds the RNN state as two bf16 terms, hi = bf16(s) then
+// lo = bf16(s - hi), both multiplied by the same C fragments, so the product
+// carries the fp32 state to within 2^-17 of each element.
+//
+// The loads are pipelined by specialised waves.  One workgroup per CU walks the 128-column tiles t = blockIdx.x, +gridDim.x, ...
+// in 64-column stages; four loader waves copy each stage's C rows and U tile
+// from HBM straight into LDS (global_load_lds, 16 bytes per lane, no
+// registers) two stages ahead of eight compute waves, and every wave meets
+// once per stage at a barrier.  A loader wave issues only these copies, so its
+// vmcnt counts them in order and "all but the newest stage done" is an exact
+// wait.  Compute wave w owns requests [m0 + 16w, m0 + 16w + 16) and keeps
+// their A rows (the B operand) in registers for the whole step; the product is
+// taken transposed, G^T = C rows . A^T, so that accumulator register i of lane
+// l holds vocabulary 16mb + 4(l/16) + i of request l%16 and the epilogue reads
+// U and writes L straight from registers.
+//
+// LDS per stage: C rows [64][kdim] bf16 with the 16-byte chunks of row j
+// XOR-swizzled by the low bits of j (conflict-free fragment reads), then the U
+// tile [128 requests][64] bf16 with chunks swizzled by request.
+constexpr int kWsCompute = 8;
+constexpr int kWsLoaders = 4;
+constexpr int kWsThreads = (kWsCompute + kWsLoaders) * 64;
+constexpr int kSubN = 64;
+constexpr int kStages = 3;
+constexpr int kStageC = kSubN * kMaxRank * 2;
+constexpr int kStageU = kTileM * kSubN * 2;
+constexpr int kStageBytes = kStageC + kStageU;
+constexpr int kWsLds = kStages * kStageBytes;
+static_assert(kWsCompute * 16 == kTileM, "one 16-request block per compute wave");
+static_assert(kStageU == 4 * kWsLoaders * 1024, "four 1 KB copies per loader wave for U");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {  // kb + 4 copies per stage, kb = kdim / 32 in 1..8
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// Chunk swizzle of the C rows: XOR with the low bits of the row, within the
+// largest power-of-two group (at most 16) that divides the chunks per row.
+__device__ __forceinline__ int c_swz(int row, int cpr) {
+  const int p2 = cpr & -cpr;
+  return row & ((p2 < 16 ? p2 : 16) - 1);
+}
+
 template <int NSPLIT>
-__global__ __launch_bounds__(kThreads, 2) void k_markov_bias(
+__global__ __launch_bounds__(kWsThreads) void k_head_bias(
     int R, int gamma, int k, int V, int kdim, float c, const uint16_t* __restrict__ U,
     const uint16_t* __restrict__ Ct, size_t ct_stride, const uint16_t* __restrict__ Ag,
     uint16_t* __restrict__ q_logits, float2* __restrict__ partial, int n_tiles) {
-  // LDS: the A rows during the GEMM, then the fp32 output tile.
-  constexpr int kAbytes = kTileM * (kMaxRank + kApad) * 2;
-  constexpr int kGbytes = kTileM * (kTileN + kGpad) * 4;
-  constexpr int kEpiPasses = kTileM / 16;
-  constexpr int kAPerThread = kTileM * (kMaxRank / 8) / kThreads;
-  __shared__ __align__(16) unsigned char lds[kAbytes > kGbytes ? kAbytes : kGbytes];
-  uint16_t* sA = (uint16_t*)lds;
-  float* sG = (float*)lds;
-
+  extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x;
-  const int n0 = tile * kTileN;
   const int m0 = blockIdx.y * kTileM;
-  const int arow = NSPLIT * kdim;  // bf16 per A row
-  const int lda = arow + kApad;
-  const int kb = kdim / 32;        // K steps of the C fragments
+  const int kb = kdim / 32;
+  const int cpr = kdim / 8;  // 16-byte chunks per C row
   const uint16_t* Ck = Ct + (size_t)(k - 1) * ct_stride;
+  // stages of this workgroup: two per tile it owns
+  const int my_tiles = blockIdx.x < n_tiles ? (n_tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int H = 2 * my_tiles;
 
-  // Every HBM read of the workgroup is issued before the first wait: the A
-  // rows (needed first), the B fragments, then the U tile for the epilogue.
-  const int vec_per_row = arow / 8;
-  const int total = kTileM * vec_per_row;
-  uint4 gat[kAPerThread];
-#pragma unroll
-  for (int i = 0; i < kAPerThread; ++i) {
-    const int idx = tid + i * kThreads;
-    const int row = idx / vec_per_row;
-    gat[i] = (idx < total && m0 + row < R)
-                 ? *(const uint4*)(Ag + (size_t)(m0 + row) * arow + (idx % vec_per_row) * 8)
-                 : make_uint4(0, 0, 0, 0);
+  if (wave >= kWsCompute) {
+    // ---------------- loader waves ----------------
+    // Stage h is copied two stages ahead of its use; "stage h+1 landed" is
+    // "at most one stage's copies outstanding" because a loader wave issues
+    // nothing else.
+    const int lw = wave - kWsCompute;
+    const int group = kb + 4;  // copies per stage per loader wave
+    auto issue = [&](int h) {
+      const int t = blockIdx.x + (h >> 1) * gridDim.x;
+      const int v0 = t * kTileN + (h & 1) * kSubN;
+      unsigned char* st = lds + (h % kStages) * kStageBytes;
+      for (int ic = 0; ic < kb; ++ic) {  // C rows v0 .. v0+63
+        const int region = ic * kWsLoaders + lw;
+        const int sid = region * 64 + lane;
+        const int row = sid / cpr, ch = (sid % cpr) ^ c_swz(row, cpr);
+        const int v = min(v0 + row, V - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(Ck + (size_t)v * kdim + ch * 8),
+                                         (lds_void_t*)(st + region * 1024), 16, 0, 0);
+      }
+      for (int iu = 0; iu < 4; ++iu) {  // U tile: 128 requests x 64 columns
+        const int region = iu * kWsLoaders + lw;
+        const int sid = region * 64 + lane;
+        const int req = sid >> 3, ch = (sid & 7) ^ (req & 7);
+        const int r = min(m0 + req, R - 1);
+        const int v = v0 + ch * 8 < V ? v0 + ch * 8 : 0;
+        __builtin_amdgcn_global_load_lds((const void*)(U + ((size_t)r * gamma + (k - 1)) * V + v),
+                                         (lds_void_t*)(st + kStageC + region * 1024), 16, 0, 0);
+      }
+    };
+    if (H > 0) issue(0);
+    if (H > 1) issue(1);
+    if (H > 1) wait_vmcnt_rt(group); else wait_vmcnt<0>();  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    for (int h = 0; h < H; ++h) {
+      if (h + 2 < H) {
+        issue(h + 2);
+        wait_vmcnt_rt(group);  // stage h+1 landed (h+2 may still be in flight)
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+    }
+    return;
   }
-  // B fragments: lane l holds column (l % 16) of its 16-column block,
-  // K values [32*ks + 8*(l/16), +8).
-  uint4 bfrag[2][kMaxRank / 32];
+
+  // ---------------- compute waves ----------------
+  const int rl = lane & 15, q = lane >> 4;
+  const int req = wave * 16 + rl;
+  const int r = m0 + req;
+  const bool rvalid = r < R;
+  const size_t urow = ((size_t)(rvalid ? r : 0) * gamma + (k - 1)) * V;
+  uint4 agf[NSPLIT][kMaxRank / 32];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int col = n0 + wave * 32 + nb * 16 + (lane & 15);
+  for (int sp = 0; sp < NSPLIT; ++sp)
+#pragma unroll
+    for (int ks = 0; ks < kMaxRank / 32; ++ks)
+      agf[sp][ks] = (rvalid && ks < kb)
+                        ? *(const uint4*)(Ag + (size_t)r * NSPLIT * kdim + (sp * kb + ks) * 32 + q * 8)
+                        : make_uint4(0, 0, 0, 0);
+  __syncthreads();  // stage 0 landed
+  float pm = kNegInf, ps = 0.0f;  // the first half's partial of the current tile
+  for (int h = 0; h < H; ++h) {
+    const int t = blockIdx.x + (h >> 1) * gridDim.x;
+    const int v0 = t * kTileN + (h & 1) * kSubN;
+    const unsigned char* st = lds + (h % kStages) * kStageBytes;
+    floatx4 acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kMaxRank / 32; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ks < kb && col < V) v = sdv::ld_nt(Ck + (size_t)col * kdim + ks * 32 + (lane >> 4) * 8);
-      bfrag[nb][ks] = v;
-    }
-  }
-  // U for the epilogue: 16 threads per row, 8 columns each, 16 rows per pass
-  const int seg = tid & 15;
-  const int ecol = n0 + seg * 8;
-  uint4 upre[kEpiPasses];
+      if (ks < kb) {
+        uint4 a[4];  // the four row blocks' fragments, read together
 #pragma unroll
-  for (int pass = 0; pass < kEpiPasses; ++pass) {
-    const int r = m0 + pass * 16 + (tid >> 4);
-    upre[pass] = (r < R && ecol < V) ? sdv::ld_nt(U + ((size_t)r * gamma + (k - 1)) * V + ecol)
-                                     : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < kAPerThread; ++i) {
-    const int idx = tid + i * kThreads;
-    if (idx < total) *(uint4*)(sA + (idx / vec_per_row) * lda + (idx % vec_per_row) * 8) = gat[i];
-  }
-  __syncthreads();
-
-  floatx4 acc[8][2];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int ks = 0; ks < kMaxRank / 32; ++ks) {
-    if (ks < kb) {
-#pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp) {
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          const uint4 av = *(const uint4*)(sA + (mb * 16 + (lane & 15)) * lda + (sp * kb + ks) * 32 +
-                                           (lane >> 4) * 8);
-          const bf16x8 a = as_bf16x8(av);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bfrag[nb][ks]),
-                                                                  acc[mb][nb], 0, 0, 0);
+        for (int mb = 0; mb < 4; ++mb) {
+          const int row = mb * 16 + rl;
+          const int ch = (ks * 4 + q) ^ c_swz(row, cpr);
+          a[mb] = *(const uint4*)(st + (row * cpr + ch) * 16);
         }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int sp = 0; sp < NSPLIT; ++sp)
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[mb]), as_bf16x8(agf[sp][ks]),
+                                                              acc[mb], 0, 0, 0);
       }
     }
-  }
-  __syncthreads();  // A rows no longer needed: reuse LDS for the output tile
-
-  // accumulator (mb, nb), register i: row mb*16 + 4*(lane/16) + i, column lane%16
-  const int ldg = kTileN + kGpad;
+    // epilogue: L = bf16(U + G) for vocabulary v0 + 16mb + 4q .. +3 of request r
+    uint2 us[4];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sG[(mb * 16 + (lane >> 4) * 4 + i) * ldg + wave * 32 + nb * 16 + (lane & 15)] = acc[mb][nb][i];
-  __syncthreads();
-
-  // Epilogue: L = bf16(U + G), stored; per-(row, tile) partial (max, sum).
-  // The 16 threads of a row are one DPP row of the wave.
-#pragma unroll
-  for (int pass = 0; pass < kEpiPasses; ++pass) {
-    const int mr = pass * 16 + (tid >> 4);
-    const int r = m0 + mr;
-    const bool live = (r < R) && (ecol < V);
-    const uint4 u = upre[pass];
-    const float4 g0 = *(const float4*)(sG + mr * ldg + seg * 8);
-    const float4 g1 = *(const float4*)(sG + mr * ldg + seg * 8 + 4);
-    uint4 o;
-    o.x = pack_bf16_rne(sdv::bf16lo(u.x) + g0.x, sdv::bf16hi(u.x) + g0.y);
-    o.y = pack_bf16_rne(sdv::bf16lo(u.y) + g0.z, sdv::bf16hi(u.y) + g0.w);
-    o.z = pack_bf16_rne(sdv::bf16lo(u.z) + g1.x, sdv::bf16hi(u.z) + g1.y);
-    o.w = pack_bf16_rne(sdv::bf16lo(u.w) + g1.z, sdv::bf16hi(u.w) + g1.w);
-    const float vals[8] = {sdv::bf16lo(o.x), sdv::bf16hi(o.x), sdv::bf16lo(o.y), sdv::bf16hi(o.y),
-                           sdv::bf16lo(o.z), sdv::bf16hi(o.z), sdv::bf16lo(o.w), sdv::bf16hi(o.w)};
-    float m = kNegInf;
-    if (live) {
-      sdv::st_nt(q_logits + ((size_t)r * gamma + (k - 1)) * V + ecol, o);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, vals[e]);
+    for (int mb = 0; mb < 4; ++mb) {
+      const int col = mb * 16 + q * 4;
+      const int ch = (col >> 3) ^ (req & 7);
+      us[mb] = *(const uint2*)(st + kStageC + (req * 8 + ch) * 16 + (col & 7) * 2);
     }
-    // row partial over the 16 lanes of this row: max, then sum relative to it
-    m = row16_max(m);
+    float vals[4][4];
+    float m = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int col = mb * 16 + q * 4;
+      const uint2 u = us[mb];
+      uint2 o;
+      o.x = pack_bf16_rne(sdv::bf16lo(u.x) + acc[mb][0], sdv::bf16hi(u.x) + acc[mb][1]);
+      o.y = pack_bf16_rne(sdv::bf16lo(u.y) + acc[mb][2], sdv::bf16hi(u.y) + acc[mb][3]);
+      vals[mb][0] = sdv::bf16lo(o.x);
+      vals[mb][1] = sdv::bf16hi(o.x);
+      vals[mb][2] = sdv::bf16lo(o.y);
+      vals[mb][3] = sdv::bf16hi(o.y);
+      if (rvalid && v0 + col < V) {
+        *(uint2*)(q_logits + urow + v0 + col) = o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, vals[mb][i]);
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
     const float ref = exp_ref(m, c);
     float s = 0.0f;
-    if (live) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += sdv::fast_exp2(fmaf(vals[e], c, -ref));
+    for (int mb = 0; mb < 4; ++mb) {
+      if (rvalid && v0 + mb * 16 + q * 4 < V) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += sdv::fast_exp2(fmaf(vals[mb][i], c, -ref));
+      }
     }
-    s = row16_sum(s);
-    if (seg == 0 && r < R) partial[(size_t)r * n_tiles + tile] = make_float2(m, s);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if ((h & 1) == 0) {
+      pm = m;
+      ps = s;
+    } else if (q == 0 && rvalid) {  // both halves of tile t: one partial
+      const float M = fmaxf(pm, m);
+      const float REF = exp_ref(M, c);
+      float S = 0.0f;
+      if (ps != 0.0f) S += ps * sdv::fast_exp2(exp_ref(pm, c) - REF);
+      if (s != 0.0f) S += s * sdv::fast_exp2(ref - REF);
+      partial[(size_t)r * n_tiles + t] = make_float2(M, S);
+    }
+    __syncthreads();  // this stage is consumed; the loaders may refill it
   }
 }
 
@@ -513,11 +586,16 @@ int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_st
              const float* hdot, float2* partial, const NextRows& nr, int32_t* tokens,
              uint16_t* q_logits, float* conf, int32_t* status) {
   const int n_tiles = (V + kTileN - 1) / kTileN;
-  const dim3 grid_bias(n_tiles, (R + kTileM - 1) / kTileM);
+  int dev = 0, n_cu = 0;
+  SDV_TRY_LAUNCH(hipGetDevice(&dev));
+  SDV_TRY_LAUNCH(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  SDV_TRY_LAUNCH(hipFuncSetAttribute((const void*)k_head_bias<NSPLIT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kWsLds));
+  const dim3 grid_bias(std::min(n_tiles, std::max(n_cu, 1)), (R + kTileM - 1) / kTileM);
   for (int k = 1; k <= gamma; ++k) {
-    SDV_TRY_LAUNCH(sdv::launch(k_markov_bias<NSPLIT>, grid_bias, dim3(kThreads), 0, stream, R, gamma,
-                               k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag, q_logits,
-                               partial, n_tiles));
+    SDV_TRY_LAUNCH(sdv::launch(k_head_bias<NSPLIT>, grid_bias, dim3(kWsThreads), kWsLds, stream, R,
+                               gamma, k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag,
+                               q_logits, partial, n_tiles));
     SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT == 2>, dim3(R), dim3(kThreads), 0, stream, gamma,
                                k, V, H, rank_e, c, seed, pos0, x0, E, w, hdot,
                                (const float2*)partial, n_tiles, (const uint16_t*)q_logits, nr, tokens,
