@@ -348,8 +348,7 @@ __device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, floa
       ((uint4*)(nr.Ag + (size_t)r * nr.rank))[v] =
           valid ? ((const uint4*)(Anext + (size_t)tok * nr.rank))[v] : make_uint4(0, 0, 0, 0);
   } else {
-    const int d = nr.rank;
-    for (int i = tid; i < d; i += kThreads) s_s[i] = nr.state[(size_t)r * d + i];
+    const int d = nr.rank;  // s_s holds this request's state (loaded by the caller)
     __syncthreads();
     for (int o = tid; o < d; o += kThreads) {
       const uint16_t* wr = nr.W + (size_t)o * d;
@@ -371,6 +370,9 @@ __device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, floa
   }
 }
 
+// Critical path: the tile partials and x_{k-1} (one round trip), the crossing
+// tile's logits and E[x_{k-1}] (a second, overlapped), the next step's row
+// (a third).  The confidence is reduced while the tile's logits are in flight.
 template <bool RNN>
 __global__ __launch_bounds__(kThreads) void k_markov_select(
     int gamma, int k, int V, int H, int rank_e, float c, uint64_t seed,
@@ -381,14 +383,16 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     float* __restrict__ conf, int32_t* __restrict__ status) {
   __shared__ float s_s[kMaxRank];
   __shared__ float s_red[kThreads / 64];
+  __shared__ float s_rede[kThreads / 64];
   __shared__ double s_redd[kThreads / 64];
   __shared__ int s_tile;
   __shared__ double s_tgt;
+  __shared__ float s_tref;
   __shared__ int s_tok, s_claim;
 
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int xp = (k == 1) ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
-  // this thread's run of tile partials, requested before the confidence work
+  // this thread's run of tile partials
   const float2* pp = partial + (size_t)r * n_tiles;
   const int per = (n_tiles + kThreads - 1) / kThreads;
   const int t0 = tid * per;
@@ -398,23 +402,16 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   for (int i = 0; i < kPre; ++i)
     pre[i] = (i < per && t0 + i < n_tiles) ? pp[t0 + i] : make_float2(kNegInf, 0.0f);
   auto part = [&](int i) { return i < kPre ? pre[i] : pp[t0 + i]; };
+  if constexpr (RNN) {  // the state the next step advances
+    for (int i = tid; i < nr.rank; i += kThreads) s_s[i] = nr.state[(size_t)r * nr.rank + i];
+  }
   const bool xvalid = xp >= 0 && xp < V;
   int st = (k == 1) ? 0 : status[r];
   if (!xvalid) st |= SD_ST_BAD_TOKEN;
-
-  // confidence of position k: sigmoid(w_h . h_k + w_e . E[x_{k-1}])
+  // the confidence's embedding term, consumed after the tile is found
   float e = 0.0f;
   if (xvalid)
     for (int i = tid; i < rank_e; i += kThreads) e += w[H + i] * sdv::bf16_to_f32(E[(size_t)xp * rank_e + i]);
-  e = sdv::wave_sum(e);
-  if (lane == 0) s_red[wave] = e;
-  __syncthreads();
-  if (tid == 0) {
-    float z = hdot[(size_t)r * gamma + (k - 1)];
-    for (int ww = 0; ww < kThreads / 64; ++ww) z += s_red[ww];
-    conf[(size_t)r * gamma + (k - 1)] = 1.0f / (1.0f + expf(-z));
-  }
-  __syncthreads();
 
   // Combine the tile partials.  Thread t owns a contiguous run of tiles.
   float M = kNegInf;
@@ -427,15 +424,15 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   __syncthreads();
   M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float REF = exp_ref(M, c);
+  auto tile_mass = [&](float2 q) {
+    return q.y != 0.0f ? (double)q.y * exp2((double)exp_ref(q.x, c) - (double)REF) : 0.0;
+  };
   double own = 0.0;
-  for (int i = 0; i < per; ++i) {
-    if (t0 + i < n_tiles) {
-      const float2 q = part(i);
-      if (q.y != 0.0f) own += (double)q.y * exp2((double)exp_ref(q.x, c) - (double)REF);
-    }
-  }
+  for (int i = 0; i < per; ++i)
+    if (t0 + i < n_tiles) own += tile_mass(part(i));
   const double incl = sdv::wave_incl_scan_d(own, lane);
   if (lane == 63) s_redd[wave] = incl;
+  if (tid == 0) { s_tile = -1; s_tok = -1; s_claim = 0x7FFFFFFF; }
   __syncthreads();
   double excl = incl - own;
   double Z = 0.0;
@@ -443,12 +440,70 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     if (ww < wave) excl += s_redd[ww];
     Z += s_redd[ww];
   }
-  if (tid == 0) { s_tile = -1; s_tok = -1; s_claim = 0x7FFFFFFF; }
-  __syncthreads();
 
   int bad = 0;
   if (isnan(M) || isnan(Z) || M == __builtin_huge_valf()) bad = SD_ST_NONFINITE;
   else if (M == kNegInf) bad = SD_ST_ZERO_Z;
+  const int64_t pbase = pos0 ? pos0[r] : 0;
+  const double u = sdv::uniform24(seed, (uint64_t)r, (uint64_t)(pbase + k), 0);
+  const double target = u * Z;
+  if (!bad) {
+    // the thread whose tile run contains the crossing walks its tiles (the
+    // lowest such thread, should rounding make two runs claim it)
+    const bool claims = excl <= target && excl + own > target;
+    if (claims) atomicMin(&s_claim, tid);
+    __syncthreads();
+    if (tid == s_claim) {
+      double cum = excl;
+      for (int i = 0; i < per && t0 + i < n_tiles; ++i) {
+        const float2 q = part(i);
+        const double s = tile_mass(q);
+        if (cum + s > target && s > 0.0) {
+          s_tile = t0 + i;
+          s_tgt = target - cum;
+          s_tref = exp_ref(q.x, c);
+          break;
+        }
+        cum += s;
+      }
+    }
+    __syncthreads();
+    if (s_tile < 0) {  // rounding pushed the target past the end: last tile with mass
+      if (tid == 0) {
+        for (int t = n_tiles - 1; t >= 0; --t)
+          if (pp[t].y > 0.0f) {
+            s_tile = t;
+            s_tref = exp_ref(pp[t].x, c);
+            break;
+          }
+        s_tgt = __builtin_huge_val();
+      }
+      __syncthreads();
+    }
+  }
+  const int tile = bad ? -1 : s_tile;
+
+  // wave 0 requests the tile's 128 logits (2 per lane) ...
+  const size_t rowoff = ((size_t)r * gamma + (k - 1)) * V;
+  const int n0 = tile * kTileN;
+  float lg[2] = {0.0f, 0.0f};
+  if (wave == 0 && tile >= 0) {
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int idx = n0 + lane * 2 + e2;
+      if (idx < V) lg[e2] = sdv::bf16_to_f32(q_logits[rowoff + idx]);
+    }
+  }
+  // ... while every wave finishes the confidence of position k:
+  // sigmoid(w_h . h_k + w_e . E[x_{k-1}])
+  e = sdv::wave_sum(e);
+  if (lane == 0) s_rede[wave] = e;
+  __syncthreads();
+  if (tid == 0) {
+    float z = hdot[(size_t)r * gamma + (k - 1)];
+    for (int ww = 0; ww < kThreads / 64; ++ww) z += s_rede[ww];
+    conf[(size_t)r * gamma + (k - 1)] = 1.0f / (1.0f + expf(-z));
+  }
   if (bad) {
     if (tid == 0) {
       tokens[(size_t)r * gamma + (k - 1)] = -1;
@@ -458,59 +513,18 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     return;
   }
 
-  const int64_t pbase = pos0 ? pos0[r] : 0;
-  const double u = sdv::uniform24(seed, (uint64_t)r, (uint64_t)(pbase + k), 0);
-  const double target = u * Z;
-  // the thread whose tile run contains the crossing walks its tiles (the
-  // lowest such thread, should rounding make two runs claim it)
-  const bool claims = excl <= target && excl + own > target;
-  if (claims) atomicMin(&s_claim, tid);
-  __syncthreads();
-  if (tid == s_claim) {
-    double cum = excl;
-    for (int i = 0; i < per && t0 + i < n_tiles; ++i) {
-      const float2 q = pp[t0 + i];
-      const double s = q.y != 0.0f ? (double)q.y * exp2((double)exp_ref(q.x, c) - (double)REF) : 0.0;
-      if (cum + s > target && s > 0.0) {
-        s_tile = t0 + i;
-        s_tgt = target - cum;
-        break;
-      }
-      cum += s;
-    }
-  }
-  __syncthreads();
-  int tile = s_tile;
-  double tgt_in = s_tgt;
-  if (tile < 0) {  // rounding pushed the target past the end: last tile with mass
-    if (tid == 0) {
-      for (int t = n_tiles - 1; t >= 0; --t)
-        if (pp[t].y > 0.0f) { s_tile = t; break; }
-      s_tgt = __builtin_huge_val();
-    }
-    __syncthreads();
-    tile = s_tile;
-    tgt_in = s_tgt;
-  }
-
-  // rescan the tile's 128 logits with wave 0: 2 per lane, weights relative to
-  // the tile's own reference, scaled into the global frame.
+  // rescan the tile's logits: weights relative to the tile's own reference,
+  // scaled into the global frame
   if (wave == 0 && tile >= 0) {
-    const float2 q = pp[tile];
-    const float tref = exp_ref(q.x, c);
+    const float tref = s_tref;
     const double scale = exp2((double)tref - (double)REF);
-    const int n0 = tile * kTileN;
-    const size_t rowoff = ((size_t)r * gamma + (k - 1)) * V;
+    const double tgt_in = s_tgt;
     double wv[2];
     int idx[2];
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       idx[e2] = n0 + lane * 2 + e2;
-      wv[e2] = 0.0;
-      if (idx[e2] < V) {
-        const float L = sdv::bf16_to_f32(q_logits[rowoff + idx[e2]]);
-        wv[e2] = (double)sdv::fast_exp2(fmaf(L, c, -tref)) * scale;
-      }
+      wv[e2] = idx[e2] < V ? (double)sdv::fast_exp2(fmaf(lg[e2], c, -tref)) * scale : 0.0;
     }
     const double lsum = wv[0] + wv[1];
     const double li = sdv::wave_incl_scan_d(lsum, lane);
