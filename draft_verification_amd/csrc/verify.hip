@@ -43,10 +43,12 @@ constexpr int kBlk = 1024;                          // elements per residual blo
 constexpr int kChunkBlocks = kChunk / kBlk;         // = kFinWaves: one block per wave
 constexpr int kMaxSlots = 2 * SD_MAX_GAMMA + 1;
 constexpr int kStagedParts = 4096;                  // partials of one request staged in LDS
+constexpr int kLdsBlocks = 2048;                    // residual block sums kept in LDS (V <= 2M)
 constexpr int kAlphaThreads = 256;
 constexpr int kNone = 0x7FFFFFFF;
 static_assert(kChunkBlocks == kFinWaves, "a bonus chunk is rescanned one block per wave");
 static_assert(sdv::kMaxChunks <= kFinThreads, "chunk locate assumes one chunk per thread");
+static_assert(SD_MAX_GAMMA < kFinThreads, "one accept test per thread");
 
 struct VerifyArgs {
   const char* tgt;
@@ -84,20 +86,21 @@ __device__ __forceinline__ int row_status(float M, double Z) {
 }
 
 // Weight of one element of the correction draw: residual max(0, p - q)
-// (kind 1) or the unnormalised target law 2^(x*c - ref) (kind 2); fp64 from
-// fp32 exponentials.
-__device__ __forceinline__ double draw_weight(float xt, float xd, int kind, float c, float mct,
-                                              double izt, float mcd, double izd) {
-  const double et = (double)sdv::fast_exp2(fmaf(xt, c, -mct));
+// (kind 1) or the unnormalised target law 2^(x*c - ref) (kind 2), in fp32
+// from fp32 exponentials (their rounding already bounds the accuracy); every
+// sum of weights is taken in fp64.
+__device__ __forceinline__ float draw_weight(float xt, float xd, int kind, float c, float mct,
+                                             float izt, float mcd, float izd) {
+  const float et = sdv::fast_exp2(fmaf(xt, c, -mct));
   if (kind != 1) return et;
-  const double ed = (double)sdv::fast_exp2(fmaf(xd, c, -mcd));
-  return fmax(0.0, et * izt - ed * izd);
+  const float ed = sdv::fast_exp2(fmaf(xd, c, -mcd));
+  return fmaxf(0.0f, fmaf(et, izt, -(ed * izd)));
 }
 
 struct DrawParams {
   int kind;
   float c, mct, mcd;
-  double izt, izd;
+  float izt, izd;  // fp32(1 / Z) of the target and draft rows (kind 1)
 };
 
 // One wave scans one 1024-element block held in registers (lane l holds
@@ -119,7 +122,7 @@ __device__ int wave_block_scan(const uint4 (&tv)[VL], const uint4 (&dv)[VL], int
     double vs = 0.0;
 #pragma unroll
     for (int e = 0; e < VT::kElems; ++e) {
-      const double w = draw_weight(xt[e], xd[e], dp.kind, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
+      const double w = (double)draw_weight(xt[e], xd[e], dp.kind, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
       vs += w;
       if (w > 0.0) lst = (vbase + k * 64 + lane) * VT::kElems + e;
     }
@@ -138,7 +141,7 @@ __device__ int wave_block_scan(const uint4 (&tv)[VL], const uint4 (&dv)[VL], int
       VT::unpack(dv[k], xd);
       double cc = c0;
       for (int e = 0; e < VT::kElems; ++e) {
-        cc += draw_weight(xt[e], xd[e], dp.kind, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
+        cc += (double)draw_weight(xt[e], xd[e], dp.kind, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
         if (cc > rem) {
           hit = (vbase + k * 64 + lane) * VT::kElems + e;
           break;
@@ -174,6 +177,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   __shared__ double sZ[kMaxSlots];
   __shared__ float2 sPart[kStagedParts];
   __shared__ double s_incl[kFinThreads];
+  __shared__ double s_bs[kLdsBlocks];
   __shared__ double s_w[kFinWaves];
   __shared__ int s_st, s_jstar, s_zero_q_upto, s_owner, s_blk, s_tok, s_last;
   __shared__ double s_rem;
@@ -188,6 +192,20 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
     s_jstar = L + 1;
     s_zero_q_upto = kNone;
     s_owner = kNone;
+  }
+
+  // The accept tests' operands (thread j-1 tests position j: the drafted
+  // token and its two logits) are requested first, then the partials.
+  const int32_t* drafts = a.draft_tokens + (size_t)r * gmax;
+  const int jt = tid + 1;
+  int xj = -1;
+  float ltj = 0.0f, ldj = 0.0f;
+  if (jt <= L) {
+    xj = drafts[jt - 1];
+    if (xj >= 0 && xj < V) {
+      ltj = VT::at(a.tgt + ((int64_t)a.tgt_row0[r] + (jt - 1)) * a.ld_bytes, xj);
+      ldj = VT::at(a.drf + ((int64_t)a.drf_row0[r] + (jt - 1)) * a.ld_bytes, xj);
+    }
   }
 
   // Stage the partials of the batch rows (target slots 0..L, then draft slots
@@ -252,18 +270,15 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
 
   // every accept test at once; the chain stops at the first rejection
   const int64_t pbase = a.pos0 ? a.pos0[r] : 0;
-  const int32_t* drafts = a.draft_tokens + (size_t)r * gmax;
-  for (int j = tid + 1; j <= L; j += kFinThreads) {
-    const int x = drafts[j - 1];
+  if (jt <= L) {
+    const int j = jt, x = xj;
     bool reject;
     if (x < 0 || x >= V) {
       reject = true;
     } else {
-      const char* trow = a.tgt + ((int64_t)a.tgt_row0[r] + (j - 1)) * a.ld_bytes;
-      const char* drow = a.drf + ((int64_t)a.drf_row0[r] + (j - 1)) * a.ld_bytes;
       const int ts = j - 1, ds = gmax + j;
-      const double p = exp2((double)VT::at(trow, x) * (double)c - (double)sRef[ts]) / sZ[ts];
-      const double q = exp2((double)VT::at(drow, x) * (double)c - (double)sRef[ds]) / sZ[ds];
+      const double p = exp2((double)ltj * (double)c - (double)sRef[ts]) / sZ[ts];
+      const double q = exp2((double)ldj * (double)c - (double)sRef[ds]) / sZ[ds];
       if (a.probe_probs) {
         a.probe_probs[((size_t)r * gmax + (j - 1)) * 2 + 0] = (float)p;
         a.probe_probs[((size_t)r * gmax + (j - 1)) * 2 + 1] = (float)q;
@@ -301,9 +316,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   dp.kind = rejected ? 1 : 2;
   dp.c = c;
   dp.mct = sRef[tslot];
-  dp.izt = 1.0 / sZ[tslot];
+  dp.izt = (float)(1.0 / sZ[tslot]);
   dp.mcd = rejected ? sRef[gmax + jstar] : 0.0f;
-  dp.izd = rejected ? 1.0 / sZ[gmax + jstar] : 1.0;
+  dp.izd = rejected ? (float)(1.0 / sZ[gmax + jstar]) : 1.0f;
   const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
   const int nvec = V / VT::kElems;
   const uint4* tp = (const uint4*)trow;
@@ -314,25 +329,22 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   double target = 0.0;
   if (dp.kind == 1) {
     // Residual mass per block: wave w streams blocks w, w + 16, ... with the
-    // next block's loads issued before the current block is summed.
+    // next block's loads issued before the current block is summed.  The
+    // block sums stay in LDS when they fit.
+    double* bs = n_blk <= kLdsBlocks ? s_bs : bsum;
     uint4 ct[VL], cd[VL];
     auto load = [&](int b, uint4 (&t)[VL], uint4 (&d)[VL]) {
 #pragma unroll
       for (int k = 0; k < VL; ++k) {
-        const int v = b * kBlkVec + k * 64 + lane;
+        const int v = b * kBlkVec + k * 64 + lane;  // v < nvec implies b < n_blk
         t[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
         d[k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
       }
     };
-    if (wave < n_blk) load(wave, ct, cd);
+    load(wave, ct, cd);
     for (int b = wave; b < n_blk; b += kFinWaves) {
       uint4 nt[VL], nd[VL];
-      if (b + kFinWaves < n_blk) {
-        load(b + kFinWaves, nt, nd);
-      } else {
-#pragma unroll
-        for (int k = 0; k < VL; ++k) nt[k] = nd[k] = ninf;
-      }
+      load(b + kFinWaves, nt, nd);
       double acc = 0.0;
 #pragma unroll
       for (int k = 0; k < VL; ++k) {
@@ -341,10 +353,10 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
         VT::unpack(cd[k], xd);
 #pragma unroll
         for (int e = 0; e < VT::kElems; ++e)
-          acc += draw_weight(xt[e], xd[e], 1, c, dp.mct, dp.izt, dp.mcd, dp.izd);
+          acc += (double)draw_weight(xt[e], xd[e], 1, c, dp.mct, dp.izt, dp.mcd, dp.izd);
       }
       acc = sdv::wave_sum_d(acc);
-      if (lane == 0) bsum[b] = acc;
+      if (lane == 0) bs[b] = acc;
 #pragma unroll
       for (int k = 0; k < VL; ++k) {
         ct[k] = nt[k];
@@ -357,7 +369,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
     const int per = (n_blk + kFinThreads - 1) / kFinThreads;
     const int b0 = min(tid * per, n_blk), b1 = min(b0 + per, n_blk);
     double tot = 0.0;
-    for (int b = b0; b < b1; ++b) tot += bsum[b];
+    for (int b = b0; b < b1; ++b) tot += bs[b];
     const double incl = block_incl_scan(tot, lane, wave, s_w);
     s_incl[tid] = incl;
     __syncthreads();
@@ -371,7 +383,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
         int blk = -1, lastpos = -1;
         double rem = __builtin_huge_val();
         for (int b = b0; b < b1; ++b) {
-          const double w = bsum[b];
+          const double w = bs[b];
           if (w > 0.0) lastpos = b;
           if (acc + w > target) {
             blk = b;
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
     st |= SD_ST_ZERO_RESIDUAL;
     dp.kind = 2;
     dp.mcd = 0.0f;
-    dp.izd = 1.0;
+    dp.izd = 1.0f;
     drow = trow;
     dq = tp;
   }
