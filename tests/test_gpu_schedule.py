@@ -81,6 +81,25 @@ def test_schedule_async_chain_on_device():
     assert float(second["theta"].item()) == ref["theta"]
 
 
+@pytest.mark.parametrize("R,gmax", [(64, 16), (41, 25), (128, 16), (683, 3), (256, 16), (241, 17)])
+def test_schedule_sizes_around_the_select_layouts(R, gmax):
+    """R * gmax = 1024, 1025, 2048, 2049, 4096, 4097: the selection holds 1, 2,
+    4 or 8 sorted positions per thread; ties and ragged lengths included."""
+    g = np.random.default_rng(R * 100 + gmax)
+    for levels in (None, (0.25, 0.5, 0.75, 1.0)):
+        if levels is None:
+            conf = (1 / (1 + np.exp(-g.normal(1.0, 1.5, (R, gmax))))).astype(np.float32)
+        else:
+            conf = g.choice(np.array(levels, np.float32), (R, gmax))
+        gam = g.integers(0, gmax + 1, R).astype(np.int32)
+        sps = sps_table(R * (gmax + 1), 256, 0.08, 64).numpy()
+        for mode in MODES:
+            _check(conf, sps, mode, gam)
+            _check(conf, sps, mode)
+        _check(conf, sps, OS.CAPPED_TOPK, gam, cap=int(g.integers(0, R * gmax + 3)))
+        _check(conf, sps, OS.THRESHOLD, gam, threshold=0.3)
+
+
 def test_schedule_maximum_slots_and_subnormal_survival():
     g = np.random.default_rng(13)
     R, gmax = 1024, 16                          # R * gmax = 16384, the limit
