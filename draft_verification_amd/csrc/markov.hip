@@ -32,6 +32,7 @@ constexpr int kThreads = 256;
 constexpr int kTileN = 128;  // vocabulary columns per workgroup (4 waves x 32)
 constexpr int kTileM = 128;  // requests per workgroup
 constexpr int kMaxRank = 256;
+static_assert(kMaxRank / 2 <= kThreads, "an RNN state of d <= kMaxRank / 2: one element per thread");
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -338,8 +339,26 @@ struct NextRows {
   uint16_t* Ag;             // [R][rank] (Markov) or [R][2d] (RNN)
 };
 
+// RNN: row o = threadIdx.x of W times the state s_k in LDS (0 for o >= d).
+// It does not depend on x_k, so the select kernel takes it early.
+__device__ float rnn_w_times_state(const NextRows& nr, const float* s_s) {
+  const int o = threadIdx.x, d = nr.rank;
+  float acc = 0.0f;
+  if (o < d) {
+    const uint16_t* wr = nr.W + (size_t)o * d;
+    for (int i = 0; i < d; i += 8) {
+      const uint4 q = *(const uint4*)(wr + i);
+      acc += sdv::bf16lo(q.x) * s_s[i] + sdv::bf16hi(q.x) * s_s[i + 1] +
+             sdv::bf16lo(q.y) * s_s[i + 2] + sdv::bf16hi(q.y) * s_s[i + 3] +
+             sdv::bf16lo(q.z) * s_s[i + 4] + sdv::bf16hi(q.z) * s_s[i + 5] +
+             sdv::bf16lo(q.w) * s_s[i + 6] + sdv::bf16hi(q.w) * s_s[i + 7];
+    }
+  }
+  return acc;
+}
+
 template <bool RNN>
-__device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, float* s_s) {
+__device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, float ws) {
   const int tid = threadIdx.x;
   const bool valid = tok >= 0 && tok < V;
   if constexpr (!RNN) {
@@ -348,18 +367,9 @@ __device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, floa
       ((uint4*)(nr.Ag + (size_t)r * nr.rank))[v] =
           valid ? ((const uint4*)(Anext + (size_t)tok * nr.rank))[v] : make_uint4(0, 0, 0, 0);
   } else {
-    const int d = nr.rank;  // s_s holds this request's state (loaded by the caller)
-    __syncthreads();
-    for (int o = tid; o < d; o += kThreads) {
-      const uint16_t* wr = nr.W + (size_t)o * d;
-      float acc = 0.0f;
-      for (int i = 0; i < d; i += 8) {
-        const uint4 q = *(const uint4*)(wr + i);
-        acc += sdv::bf16lo(q.x) * s_s[i] + sdv::bf16hi(q.x) * s_s[i + 1] +
-               sdv::bf16lo(q.y) * s_s[i + 2] + sdv::bf16hi(q.y) * s_s[i + 3] +
-               sdv::bf16lo(q.z) * s_s[i + 4] + sdv::bf16hi(q.z) * s_s[i + 5] +
-               sdv::bf16lo(q.w) * s_s[i + 6] + sdv::bf16hi(q.w) * s_s[i + 7];
-      }
+    const int d = nr.rank, o = tid;  // ws = (W s_k)[o], d <= kThreads
+    if (o < d) {
+      float acc = ws;
       if (valid) acc += sdv::bf16_to_f32(nr.Es[(size_t)tok * d + o]);
       const float sn = tanhf(acc);
       nr.state[(size_t)r * d + o] = sn;
@@ -372,7 +382,8 @@ __device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, floa
 
 // Critical path: the tile partials and x_{k-1} (one round trip), the crossing
 // tile's logits and E[x_{k-1}] (a second, overlapped), the next step's row
-// (a third).  The confidence is reduced while the tile's logits are in flight.
+// (a third).  The confidence, and for the RNN head W s_k, are computed while
+// the tile's logits are in flight.
 template <bool RNN>
 __global__ __launch_bounds__(kThreads) void k_markov_select(
     int gamma, int k, int V, int H, int rank_e, float c, uint64_t seed,
@@ -494,8 +505,11 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       if (idx < V) lg[e2] = sdv::bf16_to_f32(q_logits[rowoff + idx]);
     }
   }
-  // ... while every wave finishes the confidence of position k:
+  // ... while the RNN head multiplies its state and every wave finishes the
+  // confidence of position k:
   // sigmoid(w_h . h_k + w_e . E[x_{k-1}])
+  float ws = 0.0f;
+  if constexpr (RNN) ws = rnn_w_times_state(nr, s_s);
   e = sdv::wave_sum(e);
   if (lane == 0) s_rede[wave] = e;
   __syncthreads();
@@ -509,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       tokens[(size_t)r * gamma + (k - 1)] = -1;
       status[r] = st | bad;
     }
-    if (k < gamma) next_rows<RNN>(nr, r, k, V, -1, s_s);  // no valid token to carry forward
+    if (k < gamma) next_rows<RNN>(nr, r, k, V, -1, ws);  // no valid token to carry forward
     return;
   }
 
@@ -548,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     tokens[(size_t)r * gamma + (k - 1)] = tok;
     status[r] = st;
   }
-  if (k < gamma) next_rows<RNN>(nr, r, k, V, tok, s_s);
+  if (k < gamma) next_rows<RNN>(nr, r, k, V, tok, ws);
 }
 
 // s_1 = tanh(W s_0 + E_s[x_0]) = tanh(E_s[x_0]) (s_0 = 0; no embedding term for
