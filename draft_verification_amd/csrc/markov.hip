@@ -114,8 +114,10 @@ __global__ __launch_bounds__(64) void k_gather_a(int R, int V, int rank, const u
 // lo = bf16(s - hi), both multiplied by the same C fragments, so the product
 // carries the fp32 state to within 2^-17 of each element.
 //
-// The loads are pipelined by specialised waves.  One workgroup per CU walks the 128-column tiles t = blockIdx.x, +gridDim.x, ...
-// in 64-column stages; four loader waves copy each stage's C rows and U tile
+// The loads are pipelined by specialised waves.  One workgroup per CU walks
+// the 128-column tiles t = blockIdx.x, + gridDim.x, ... (so that at any time
+// the chip sweeps C_k and U_k as one contiguous front) in 64-column stages;
+// four loader waves copy each stage's C rows and U tile
 // from HBM straight into LDS (global_load_lds, 16 bytes per lane, no
 // registers) two stages ahead of eight compute waves, and every wave meets
 // once per stage at a barrier.  A loader wave issues only these copies, so its
