@@ -361,6 +361,26 @@ def main():
     rows = R * (g + 1)
     value = rows * K / (ms_total / 1e3)
 
+    # verification alone on the scheduled (full-block) lengths, both input
+    # sets alternating: rows / t(sd_verify)
+    ells = [bufs[i][0]["ell"] for i in range(len(sets))]
+    def verify_only(i):
+        inp = sets[i % len(sets)]
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                      ells[i % len(sets)], V, inp["temperature"], inp["seed"], workspace=ws,
+                      out=bufs[i % len(sets)][1])
+    for i in range(2):
+        verify_only(i)
+    torch.cuda.synchronize()
+    v0 = torch.cuda.Event(enable_timing=True)
+    v1 = torch.cuda.Event(enable_timing=True)
+    v0.record()
+    for i in range(K):
+        verify_only(i)
+    v1.record()
+    torch.cuda.synchronize()
+    verify_us = v0.elapsed_time(v1) / K * 1e3
+
     # schedule alone (the rest of the step is verification): its kernels are
     # shorter than the host's per-call overhead, so time a captured graph
     so = bufs[0][0]
@@ -419,7 +439,11 @@ def main():
                    "input_sets": len(sets)},
         "roofline": roofline,
         "breakdown_us": {"step": round(ms_per_step * 1e3, 1), "schedule": round(sched_us, 1),
-                         "row_stats_kernel": round(k_avg * 1e3, 1)},
+                         "verify": round(verify_us, 1), "row_stats_kernel": round(k_avg * 1e3, 1)},
+        "verify_only": {"rows_per_s": round(rows / (verify_us / 1e6), 1),
+                        "hbm_frac": round(bytes_launch / (verify_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "what": "sd_verify alone on the full block (rows / t(sd_verify)); value above "
+                                "times the whole step, scheduler included"},
     }
     print("budget planner", file=sys.stderr, flush=True)
     result["budget_planner"] = bench_planner(sdv, torch, sets[0], bufs[0][1], bufs[0][0]["ell"])
