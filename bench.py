@@ -86,6 +86,18 @@ def load_traffic(bytes_per_launch):
     return t.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(inp, ell, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the same step: the
     full schedule plus verification of as many requests as fit the budget."""
@@ -119,7 +131,7 @@ def cpu_baseline(inp, ell, budget_s=12.0):
         "sample": (f"full schedule of all {R} requests ({t_sched:.2f} s) + verification of {done} of "
                    f"{R} requests ({rows_sample} target rows, {t_ver:.1f} s), scaled to the whole "
                    f"step; fp64 NumPy elementwise work runs on one thread (OMP_NUM_THREADS={threads}, "
-                   f"host reports {os.cpu_count()} CPUs)"),
+                   f"host reports {os.cpu_count()} CPUs: {cpu_model()})"),
     }
 
 
