@@ -74,6 +74,16 @@ def test_verify_vocab_beyond_one_block_per_thread():
         _full_check(inp, ell)
 
 
+def test_verify_without_drafts():
+    """gamma_max = 0: no draft rows, every request samples its one token from
+    target row 0 (the bonus draw with l = 0)."""
+    for dtype in (torch.bfloat16, torch.float32):
+        inp = _to_cuda(verify_inputs(R=6, gmax=0, V=5000, dtype=dtype, sigma_t=2.0, zipf=True, seed=83))
+        ell = torch.zeros(6, dtype=torch.int32, device="cuda")
+        gpu, _ = _full_check(inp, ell)
+        assert np.all(to_np(gpu["n_acc"]) == 0)
+
+
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
