@@ -14,13 +14,12 @@
 //                    fused with + U_k, bf16 rounding, the q_logits store and a
 //                    per-(row, 128-column tile) partial (max, sum 2^(L*c - ref));
 //                    loader waves stream C_k and U_k into LDS ahead of the
-//                    MFMA waves; the rows A_k[x_{k-1}] arrive pre-gathered
+//                    MFMA waves, which gather their rows A_k[x_{k-1}] while
+//                    the first stage loads
 //   k_markov_select  one workgroup per request: confidence of position k,
 //                    combine tile partials, locate the inverse-CDF tile,
-//                    rescan 128 logits, emit x_k, and gather A_{k+1}[x_k]
-//                    for the next step
-// plus, up front, one k_hidden_dot launch for w_h . h_k of every position and
-// one k_gather_a launch for A_1[x_0].
+//                    rescan 128 logits, emit x_k
+// plus, up front, one k_hidden_dot launch for w_h . h_k of every position.
 #include <algorithm>
 
 #include "sdv_common.h"
@@ -91,26 +90,12 @@ __global__ __launch_bounds__(kThreads) void k_hidden_dot(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Ag[r] = A_k[x_prev[r]] (rank bf16), zeros when x_prev is outside [0, V): the
-// anchor contributes no Markov bias.  Used for step 1; k_markov_select does it
-// for the following steps.
-__global__ __launch_bounds__(64) void k_gather_a(int R, int V, int rank, const uint16_t* __restrict__ Ak,
-                                                 const int32_t* __restrict__ xprev,
-                                                 uint16_t* __restrict__ Ag) {
-  const int r = blockIdx.x;
-  const int xp = xprev[r];
-  const bool valid = xp >= 0 && xp < V;
-  for (int v = threadIdx.x; v < rank / 8; v += 64)
-    ((uint4*)(Ag + (size_t)r * rank))[v] =
-        valid ? ((const uint4*)(Ak + (size_t)xp * rank))[v] : make_uint4(0, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// The bias product G = Ag . C_k (M = requests, N = vocabulary, K = kdim) with
+// The bias product G = A . C_k (M = requests, N = vocabulary, K = kdim) with
 // v_mfma_f32_16x16x32_bf16, fused with + U_k, the bf16 rounding, the q_logits
 // store and one partial (max, sum 2^(L*c - ref)) per (request, 128-column
-// tile).  NSPLIT = 1: Ag[r] holds A_k[x_{k-1}] (the Markov head).  NSPLIT = 2:
-// Ag[r] holds the RNN state as two bf16 terms, hi = bf16(s) then
+// tile).  NSPLIT = 1, the Markov head: row r of A is A_k[x_{k-1}], gathered
+// from the table at the start (zeros for an invalid token).  NSPLIT = 2, the
+// RNN head: Ag[r] holds the state as two bf16 terms, hi = bf16(s) then
 // lo = bf16(s - hi), both multiplied by the same C fragments, so the product
 // carries the fp32 state to within 2^-17 of each element.
 //
@@ -175,7 +160,9 @@ template <int NSPLIT>
 __global__ __launch_bounds__(kWsThreads) void k_head_bias(
     int R, int gamma, int k, int V, int kdim, float c, const uint16_t* __restrict__ U,
     const uint16_t* __restrict__ Ct, size_t ct_stride, const uint16_t* __restrict__ Ag,
-    uint16_t* __restrict__ q_logits, float2* __restrict__ partial, int n_tiles) {
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ x0,
+    const int32_t* __restrict__ tokens, uint16_t* __restrict__ q_logits,
+    float2* __restrict__ partial, int n_tiles) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * kTileM;
@@ -238,13 +225,22 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
   const bool rvalid = r < R;
   const size_t urow = ((size_t)(rvalid ? r : 0) * gamma + (k - 1)) * V;
   uint4 agf[NSPLIT][kMaxRank / 32];
-#pragma unroll
-  for (int sp = 0; sp < NSPLIT; ++sp)
+  if (A != nullptr) {  // Markov: gather A_k[x_{k-1}] here, under the first stage's load
+    const int x = rvalid ? (k == 1 ? x0[r] : tokens[(size_t)r * gamma + (k - 2)]) : -1;
+    const bool xv = x >= 0 && x < V;  // no bias for an invalid token
+    const uint16_t* arow = A + ((size_t)(k - 1) * V + (xv ? x : 0)) * kdim;
 #pragma unroll
     for (int ks = 0; ks < kMaxRank / 32; ++ks)
-      agf[sp][ks] = (rvalid && ks < kb)
-                        ? *(const uint4*)(Ag + (size_t)r * NSPLIT * kdim + (sp * kb + ks) * 32 + q * 8)
-                        : make_uint4(0, 0, 0, 0);
+      agf[0][ks] = (xv && ks < kb) ? *(const uint4*)(arow + ks * 32 + q * 8) : make_uint4(0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int sp = 0; sp < NSPLIT; ++sp)
+#pragma unroll
+      for (int ks = 0; ks < kMaxRank / 32; ++ks)
+        agf[sp][ks] = (rvalid && ks < kb)
+                          ? *(const uint4*)(Ag + (size_t)r * NSPLIT * kdim + (sp * kb + ks) * 32 + q * 8)
+                          : make_uint4(0, 0, 0, 0);
+  }
   __syncthreads();  // stage 0 landed
   float pm = kNegInf, ps = 0.0f;  // the first half's partial of the current tile
   for (int h = 0; h < H; ++h) {
@@ -328,17 +324,13 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
 }
 
 // ---------------------------------------------------------------------------
-// The rows the next step's bias multiplies, once x_k is known (every thread
-// calls).  Markov: Ag[r] = A_{k+1}[x_k], zeros for an invalid token.  RNN:
-// s_{k+1} = tanh(W s_k + E_s[x_k]) in fp32 (no embedding term for an invalid
-// token), kept in state[r] and written to Ag[r] as its two bf16 terms.
+// The RNN head's tables and the state the next step's bias multiplies.
 struct NextRows {
-  int rank;                 // Markov: A row length; RNN: state size d
-  const uint16_t* A;        // Markov: A [gamma][V][rank]
-  const uint16_t* W;        // RNN: W [d][d]
-  const uint16_t* Es;       // RNN: E_s [V][d]
-  float* state;             // RNN: [R][d]
-  uint16_t* Ag;             // [R][rank] (Markov) or [R][2d] (RNN)
+  int rank;                 // state size d
+  const uint16_t* W;        // W [d][d]
+  const uint16_t* Es;       // E_s [V][d]
+  float* state;             // [R][d]
+  uint16_t* Ag;             // [R][2d]: the state as two bf16 terms
 };
 
 // RNN: row o = threadIdx.x of W times the state s_k in LDS (0 for o >= d).
@@ -359,33 +351,26 @@ __device__ float rnn_w_times_state(const NextRows& nr, const float* s_s) {
   return acc;
 }
 
-template <bool RNN>
-__device__ void next_rows(const NextRows& nr, int r, int k, int V, int tok, float ws) {
-  const int tid = threadIdx.x;
-  const bool valid = tok >= 0 && tok < V;
-  if constexpr (!RNN) {
-    const uint16_t* Anext = nr.A + (size_t)k * V * nr.rank;
-    for (int v = tid; v < nr.rank / 8; v += kThreads)
-      ((uint4*)(nr.Ag + (size_t)r * nr.rank))[v] =
-          valid ? ((const uint4*)(Anext + (size_t)tok * nr.rank))[v] : make_uint4(0, 0, 0, 0);
-  } else {
-    const int d = nr.rank, o = tid;  // ws = (W s_k)[o], d <= kThreads
-    if (o < d) {
-      float acc = ws;
-      if (valid) acc += sdv::bf16_to_f32(nr.Es[(size_t)tok * d + o]);
-      const float sn = tanhf(acc);
-      nr.state[(size_t)r * d + o] = sn;
-      const uint16_t hi = sdv::f32_to_bf16_rne(sn);
-      nr.Ag[(size_t)r * 2 * d + o] = hi;
-      nr.Ag[(size_t)r * 2 * d + d + o] = sdv::f32_to_bf16_rne(sn - sdv::bf16_to_f32(hi));
-    }
+// RNN, once x_k is known: s_{k+1} = tanh(W s_k + E_s[x_k]) in fp32 (no
+// embedding term for an invalid token), kept in state[r] and written to Ag[r]
+// as its two bf16 terms; ws = (W s_k)[threadIdx.x].
+__device__ void rnn_next_state(const NextRows& nr, int r, int V, int tok, float ws) {
+  const int d = nr.rank, o = threadIdx.x;  // d <= kThreads
+  if (o < d) {
+    float acc = ws;
+    if (tok >= 0 && tok < V) acc += sdv::bf16_to_f32(nr.Es[(size_t)tok * d + o]);
+    const float sn = tanhf(acc);
+    nr.state[(size_t)r * d + o] = sn;
+    const uint16_t hi = sdv::f32_to_bf16_rne(sn);
+    nr.Ag[(size_t)r * 2 * d + o] = hi;
+    nr.Ag[(size_t)r * 2 * d + d + o] = sdv::f32_to_bf16_rne(sn - sdv::bf16_to_f32(hi));
   }
 }
 
 // Critical path: the tile partials and x_{k-1} (one round trip), the crossing
-// tile's logits and E[x_{k-1}] (a second, overlapped), the next step's row
-// (a third).  The confidence, and for the RNN head W s_k, are computed while
-// the tile's logits are in flight.
+// tile's logits and E[x_{k-1}] (a second, overlapped), and for the RNN head
+// the next state (a third).  The confidence, and for the RNN head W s_k, are
+// computed while the tile's logits are in flight.
 template <bool RNN>
 __global__ __launch_bounds__(kThreads) void k_markov_select(
     int gamma, int k, int V, int H, int rank_e, float c, uint64_t seed,
@@ -525,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       tokens[(size_t)r * gamma + (k - 1)] = -1;
       status[r] = st | bad;
     }
-    if (k < gamma) next_rows<RNN>(nr, r, k, V, -1, ws);  // no valid token to carry forward
+    if (RNN && k < gamma) rnn_next_state(nr, r, V, -1, ws);  // no valid token to carry forward
     return;
   }
 
@@ -564,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     tokens[(size_t)r * gamma + (k - 1)] = tok;
     status[r] = st;
   }
-  if (k < gamma) next_rows<RNN>(nr, r, k, V, tok, ws);
+  if (RNN && k < gamma) rnn_next_state(nr, r, V, tok, ws);
 }
 
 // s_1 = tanh(W s_0 + E_s[x_0]) = tanh(E_s[x_0]) (s_0 = 0; no embedding term for
@@ -585,8 +570,8 @@ __global__ __launch_bounds__(kThreads) void k_rnn_init(int R, int V, int d, cons
   }
 }
 
-// Workspace: hdot [R][gamma] fp32, tile partials [R][n_tiles] float2, the next
-// step's A rows [R][arow] bf16, RNN state [R][d] fp32 (d = 0 for Markov).
+// Workspace: hdot [R][gamma] fp32, tile partials [R][n_tiles] float2, and for
+// the RNN head the split state [R][arow = 2d] bf16 and the state [R][d] fp32.
 size_t head_ws_bytes(int R, int gamma, int V, int arow, int d) {
   const size_t n_tiles = ((size_t)V + kTileN - 1) / kTileN;
   return sdv_align256((size_t)R * gamma * sizeof(float)) +
@@ -594,7 +579,7 @@ size_t head_ws_bytes(int R, int gamma, int V, int arow, int d) {
          sdv_align256((size_t)R * arow * sizeof(uint16_t)) +
          sdv_align256((size_t)R * d * sizeof(float));
 }
-size_t markov_ws_bytes(int R, int gamma, int V, int rank) { return head_ws_bytes(R, gamma, V, rank, 0); }
+size_t markov_ws_bytes(int R, int gamma, int V, int) { return head_ws_bytes(R, gamma, V, 0, 0); }
 size_t rnn_ws_bytes(int R, int gamma, int V, int d) { return head_ws_bytes(R, gamma, V, 2 * d, d); }
 
 // Checks shared by both heads (everything but the head's own tables).
@@ -611,7 +596,7 @@ int check_head_args(int R, int gamma, int V, int H, int rank_e, float temperatur
 // then the select kernel (which also prepares the next step's rows).
 template <int NSPLIT>
 int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_stride, float c,
-             uint64_t seed, const int64_t* pos0, const uint16_t* U, const uint16_t* Ct,
+             uint64_t seed, const int64_t* pos0, const uint16_t* U, const uint16_t* A, const uint16_t* Ct,
              const int32_t* x0, int H, const uint16_t* E, int rank_e, const float* w,
              const float* hdot, float2* partial, const NextRows& nr, int32_t* tokens,
              uint16_t* q_logits, float* conf, int32_t* status) {
@@ -624,8 +609,8 @@ int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_st
   const dim3 grid_bias(std::min(n_tiles, std::max(n_cu, 1)), (R + kTileM - 1) / kTileM);
   for (int k = 1; k <= gamma; ++k) {
     SDV_TRY_LAUNCH(sdv::launch(k_head_bias<NSPLIT>, grid_bias, dim3(kWsThreads), kWsLds, stream, R,
-                               gamma, k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag,
-                               q_logits, partial, n_tiles));
+                               gamma, k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag, A, x0,
+                               (const int32_t*)tokens, q_logits, partial, n_tiles));
     SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT == 2>, dim3(R), dim3(kThreads), 0, stream, gamma,
                                k, V, H, rank_e, c, seed, pos0, x0, E, w, hdot,
                                (const float2*)partial, n_tiles, (const uint16_t*)q_logits, nr, tokens,
@@ -668,14 +653,13 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
   p += sdv_align256((size_t)R * gamma * sizeof(float));
   float2* partial = (float2*)p;
   p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
-  NextRows nr{rank, A, nullptr, nullptr, nullptr, (uint16_t*)p};
+  const NextRows nr{rank, nullptr, nullptr, nullptr, nullptr};  // unused: no recurrent state
 
   const int rows = R * gamma;
   SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
                              rows, hdot));
-  SDV_TRY_LAUNCH(sdv::launch(k_gather_a, dim3(R), dim3(64), 0, stream, R, V, rank, A, x0, nr.Ag));
   return run_head<1>(stream, R, gamma, V, rank, (size_t)V * rank, sdv::kLog2e / temperature, seed,
-                     pos0, U, Ct, x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf,
+                     pos0, U, A, Ct, x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf,
                      status);
 }
 
@@ -714,13 +698,13 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
   p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
   uint16_t* Ag = (uint16_t*)p;
   p += sdv_align256((size_t)R * 2 * d * sizeof(uint16_t));
-  NextRows nr{d, nullptr, W, Es, (float*)p, Ag};
+  const NextRows nr{d, W, Es, (float*)p, Ag};
 
   const int rows = R * gamma;
   SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
                              rows, hdot));
   SDV_TRY_LAUNCH(sdv::launch(k_rnn_init, dim3(R), dim3(kThreads), 0, stream, R, V, d, Es, x0, nr.state,
                              nr.Ag));
-  return run_head<2>(stream, R, gamma, V, d, 0, sdv::kLog2e / temperature, seed, pos0, U, Ct, x0, H,
-                     E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf, status);
+  return run_head<2>(stream, R, gamma, V, d, 0, sdv::kLog2e / temperature, seed, pos0, U, nullptr, Ct,
+                     x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf, status);
 }
