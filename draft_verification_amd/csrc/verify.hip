@@ -638,7 +638,7 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
     return SD_EINVAL;
   const int n_ch = (V + kChunk - 1) / kChunk;
   const long long items = (long long)R * (2 * gamma_max + 1) * n_ch;
-  if (items > 0x7FFFFFFFLL) return SD_EUNSUPPORTED;
+  if (items > 0xFFFFFFFFLL / sdv::kRowThreads) return SD_EUNSUPPORTED;  // work-items of one launch
   const int64_t ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
   const float c = sdv::kLog2e / temperature;
   const char* drf = (const char*)(drf_logits ? drf_logits : tgt_logits);

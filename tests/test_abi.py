@@ -86,6 +86,8 @@ def test_verify_host_validation():
     assert _ver(nulls=("tgt",)) == _lib.SD_EINVAL
     assert _ver(nulls=("ell",)) == _lib.SD_EINVAL
     assert _ver(R=0) == _lib.SD_OK                                  # nothing to do
+    # 1024 requests x 511 rows x 64 chunks: more work-items than one launch holds
+    assert _ver(R=1024, g=255, V=1 << 20, ld=1 << 20, ws=1 << 40) == _lib.SD_EUNSUPPORTED
 
 
 def _mk(R=2, g=2, V=64, rank=32, H=8, re_=8, T=1.0, ws=1 << 20, nulls=()):
