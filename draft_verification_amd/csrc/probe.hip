@@ -42,7 +42,7 @@ extern "C" int sd_stream_read(hipStream_t stream, const void* src, long long byt
   if (!src || !sink || (((uintptr_t)src) & 15) != 0) return SD_EINVAL;
   const long long n = bytes / 16;
   const long long blocks = (n + kVecPerBlock - 1) / kVecPerBlock;
-  if (blocks > 0x7FFFFFFFLL) return SD_EUNSUPPORTED;
+  if (blocks > 0xFFFFFFFFLL / kThreads) return SD_EUNSUPPORTED;  // work-items of one launch
   SDV_TRY_LAUNCH(sdv::launch(k_stream_read, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                              (const uint4*)src, n, sink));
   return SD_OK;
