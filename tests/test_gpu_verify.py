@@ -84,6 +84,17 @@ def test_verify_without_drafts():
         assert np.all(to_np(gpu["n_acc"]) == 0)
 
 
+def test_verify_maximum_draft_length():
+    """gamma_max = 255 (the build's limit): 511 batch rows per request and up
+    to 255 accept tests at once; drafts close to the target so that long
+    prefixes are accepted."""
+    inp = _to_cuda(verify_inputs(R=3, gmax=255, V=1024, dtype=torch.bfloat16, sigma_t=2.0,
+                                 sigma_d=(0.02, 0.05), seed=84))
+    ell = torch.tensor([255, 100, 0], dtype=torch.int32, device="cuda")
+    gpu, ora = _full_check(inp, ell)
+    assert int(ora["n_acc"].max()) > 20          # the long chains are exercised
+
+
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
