@@ -47,24 +47,6 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Reductions over each 16-lane DPP row; every lane of the row gets the result.
-// Partners: xor 1, xor 2 (quad permutes), then the half-row and row mirrors.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  return fmaxf(v, dpp_f<0x140>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  return v + dpp_f<0x140>(v);
-}
 __device__ __forceinline__ float exp_ref(float m, float c) { return m == kNegInf ? 0.0f : m * c; }
 
 // ---------------------------------------------------------------------------
