@@ -95,6 +95,16 @@ def test_verify_maximum_draft_length():
     assert int(ora["n_acc"].max()) > 20          # the long chains are exercised
 
 
+def test_verify_vocab_past_the_lds_block_sums():
+    """V > 2M: the residual block sums no longer fit in LDS and go through the
+    workspace; and V = 2^24, the build's largest vocabulary (1024 chunks)."""
+    for R, g, V, seed in ((2, 2, 4_000_008, 85), (1, 1, 1 << 24, 86)):
+        inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=torch.bfloat16, sigma_t=2.0, zipf=True,
+                                     sigma_d=(1.0, 3.0), seed=seed))
+        ell = torch.full((R,), g, dtype=torch.int32, device="cuda")
+        _full_check(inp, ell)
+
+
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
