@@ -98,8 +98,9 @@ def test_verify_maximum_draft_length():
 def test_verify_vocab_past_the_lds_block_sums():
     """V > 2M: the residual block sums no longer fit in LDS and go through the
     workspace; and V = 2^24, the build's largest vocabulary (1024 chunks)."""
-    for R, g, V, seed in ((2, 2, 4_000_008, 85), (1, 1, 1 << 24, 86)):
-        inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=torch.bfloat16, sigma_t=2.0, zipf=True,
+    for R, g, V, dtype, seed in ((2, 2, 4_000_008, torch.bfloat16, 85), (2, 2, 4_000_008, torch.float32, 87),
+                                 (1, 1, 1 << 24, torch.bfloat16, 86)):
+        inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=dtype, sigma_t=2.0, zipf=True,
                                      sigma_d=(1.0, 3.0), seed=seed))
         ell = torch.full((R,), g, dtype=torch.int32, device="cuda")
         _full_check(inp, ell)
