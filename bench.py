@@ -275,11 +275,52 @@ def bench_markov(sdv, torch, steps, hip):
     ms = e0.elapsed_time(e1) / n
     hbm = (2 * g * V * rank + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # Ct + U + L + h
     flops = 2.0 * R * rank * V * g
-    return {"workload": f"R={R}, gamma={g}, V={V}, rank={rank}, H=4096, bf16",
-            "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
-            "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
-            "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
-            "launches": 2 * g + 2}
+    res = {"workload": f"R={R}, gamma={g}, V={V}, rank={rank}, H=4096, bf16",
+           "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
+           "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
+           "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
+           "launches": 2 * g + 2}
+
+    # one whole step at these sizes: draft, schedule (early stop) on the
+    # drafted confidences, verify the drafted rows against target rows with
+    # the head's (m, Z) handed to the verifier
+    from workloads import markov_targets
+    tgt, sps = markov_targets(inp["U"])
+    out["q_stats"] = torch.empty((R, g, 2), dtype=torch.float32, device=dev)
+    t0 = torch.arange(R, dtype=torch.int32, device=dev) * (g + 1)
+    d0 = torch.arange(R, dtype=torch.int32, device=dev) * g
+    so = dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+              batch=torch.empty(1, dtype=torch.int32, device=dev),
+              n_sel=torch.empty(1, dtype=torch.int32, device=dev),
+              theta=torch.empty(1, dtype=torch.float64, device=dev),
+              surv=torch.empty((R, g), dtype=torch.float32, device=dev))
+    vo = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+              tokens=torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+              status=torch.empty(R, dtype=torch.int32, device=dev))
+    sws = torch.empty(sdv.sd_schedule_workspace_size(R, g), dtype=torch.uint8, device=dev)
+    vws = torch.empty(sdv.sd_verify_workspace_size(R, g, V), dtype=torch.uint8, device=dev)
+
+    def pipeline():
+        sdv.sd_markov_draft(inp["U"], inp["A"], inp["Ct"], inp["x0"], inp["h"], inp["E"], inp["w"], 1.0,
+                            inp["seed"], workspace=ws, out=out, stats=True)
+        sch = sdv.sd_schedule(out["conf"], sps, sdv.SD_SCHED_EARLY_STOP, out=so, workspace=sws)
+        sdv.sd_verify(tgt, t0, out["q_logits"].view(R * g, V), d0, out["tokens"], sch["ell"], V, 1.0,
+                      inp["seed"] + 1, workspace=vws, out=vo, drf_stats=out["q_stats"])
+    for _ in range(2):
+        pipeline()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        pipeline()
+    e1.record()
+    torch.cuda.synchronize()
+    pms = e0.elapsed_time(e1) / n
+    B = int(so["batch"].item())
+    res["pipeline"] = {"ms_per_step": pms, "batch_rows": B,
+                       "emitted_tokens": int(vo["n_acc"].sum().item()) + R,
+                       "what": "draft (16 positions) + early-stop schedule + verify of the scheduled "
+                               "rows with the head's (m, Z) supplied; target rows seeded from U"}
+    return res
 
 
 def main():
@@ -395,6 +436,40 @@ def main():
     torch.cuda.synchronize()
     verify_us = v0.elapsed_time(v1) / K * 1e3
 
+    # the same step with each draft row's (m, Z) handed over by the drafter
+    # (the drafting heads' q_stats): the pairs are taken once, untimed, from a
+    # call that read the rows; the bandwidth pass then streams the target rows
+    # alone and the draft rows are read only at the drafted tokens and the
+    # rejected position
+    dstats = []
+    for i in range(len(sets)):
+        inp = sets[i]
+        rs = sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                           ells[i], V, inp["temperature"], inp["seed"], workspace=ws, stats=True)
+        dstats.append(rs["row_stats"][:, g + 1:, :].contiguous())
+    ref_tokens = [bufs[i][1]["tokens"].clone() for i in range(len(sets))]
+
+    def step_ds(i):
+        inp = sets[i % len(sets)]
+        so, vo = bufs[i % len(sets)]
+        sch = sdv.sd_schedule(inp["conf"], inp["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so,
+                              workspace=sws)
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                      sch["ell"], V, inp["temperature"], inp["seed"], workspace=ws, out=vo,
+                      drf_stats=dstats[i % len(sets)])
+    for i in range(len(sets)):
+        step_ds(i)
+    torch.cuda.synchronize()
+    same_tokens = all(torch.equal(bufs[i][1]["tokens"], ref_tokens[i]) for i in range(len(sets)))
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for i in range(K):
+        step_ds(i)
+    d1.record()
+    torch.cuda.synchronize()
+    ds_step_us = d0.elapsed_time(d1) / K * 1e3
+
     # schedule alone (the rest of the step is verification): its kernels are
     # shorter than the host's per-call overhead, so time a captured graph
     so = bufs[0][0]
@@ -458,6 +533,15 @@ def main():
                         "hbm_frac": round(bytes_launch / (verify_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
                         "what": "sd_verify alone on the full block (rows / t(sd_verify)); value above "
                                 "times the whole step, scheduler included"},
+        "with_drafter_stats": {
+            "rows_per_s": round(rows / (ds_step_us / 1e6), 1),
+            "us_per_step": round(ds_step_us, 1),
+            "target_bytes_hbm_frac": round(2 * V * rows / (ds_step_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_same_as_full_pass": same_tokens,
+            "what": "the same schedule+verify step with each draft row's (m, Z) supplied by the "
+                    "drafter (sd_verify drf_stats, as the drafting heads' q_stats give it): only "
+                    "the 3072 target rows are streamed; not the headline value, which reads every "
+                    "draft row too"},
     }
     print("budget planner", file=sys.stderr, flush=True)
     result["budget_planner"] = bench_planner(sdv, torch, sets[0], bufs[0][1], bufs[0][0]["ell"])

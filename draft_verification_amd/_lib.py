@@ -77,17 +77,17 @@ def lib():
     L.sd_verify_workspace_size.argtypes = [_I, _I, _I]
     L.sd_verify.restype = _I
     L.sd_verify.argtypes = [_P, _I, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P, _P,
-                            _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
     L.sd_markov_draft_workspace_size.restype = _SZ
     L.sd_markov_draft_workspace_size.argtypes = [_I, _I, _I, _I]
     L.sd_markov_draft.restype = _I
     L.sd_markov_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P,
-                                  _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
+                                  _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _SZ]
     L.sd_rnn_draft_workspace_size.restype = _SZ
     L.sd_rnn_draft_workspace_size.argtypes = [_I, _I, _I, _I]
     L.sd_rnn_draft.restype = _I
     L.sd_rnn_draft.argtypes = [_P, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P, _P, _P,
-                               _I, _P, _I, _P, _P, _P, _P, _P, _P, _SZ]
+                               _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _SZ]
     L.sd_lightspec_update.restype = _I
     L.sd_lightspec_update.argtypes = [_P, _I, _I, _P, _P, _P, ctypes.c_double, _P, _P]
     L.sd_lightspec_plan_workspace_size.restype = _SZ
@@ -180,13 +180,17 @@ def sd_verify_workspace_size(R, gmax, V):
 
 def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.0, seed=0,
               pos0=None, probe=False, stats=False, alpha=False, workspace=None, out=None,
-              stream=None, prof_events=None):
+              stream=None, prof_events=None, drf_stats=None):
     """Run verification.  tgt / drf: 2-D logit tensors (bf16 or fp32, ld =
     shape[1]); the rest int32 device tensors.  Returns a dict of device
     tensors: n_acc, tokens, status (and probe, row_stats, alpha if asked).
     prof_events: optional pair of raw hipEvent_t handles (ints) recorded
-    around the row-statistics pass."""
+    around the row-statistics pass.  drf_stats: optional [R][gamma_max][2]
+    fp32 (m, Z) of the draft rows (a drafting head's q_stats); the draft rows
+    are then read only where needed."""
     R, gmax = draft_tokens.shape
+    if drf_stats is not None and drf_stats.numel() != R * gmax * 2:
+        raise ValueError("drf_stats must hold R * gamma_max (m, Z) pairs")
     dev = tgt.device
     if tgt.dtype == torch.bfloat16:
         dt = SD_DTYPE_BF16
@@ -210,6 +214,7 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
         _stream(stream), R, gmax, int(V), ld, dt, float(temperature), int(seed) & (2**64 - 1),
         _ptr(pos0, torch.int64, "pos0"), _ptr(tgt, None, "tgt"), _ptr(tgt_row0, torch.int32, "tgt_row0"),
         _ptr(drf, None, "drf"), _ptr(drf_row0, torch.int32, "drf_row0"),
+        _ptr(drf_stats, torch.float32, "drf_stats"),
         _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(ell, torch.int32, "ell"),
         _ptr(n_acc, torch.int32), _ptr(toks, torch.int32), _ptr(status, torch.int32),
         _ptr(pp, torch.float32), _ptr(rs, torch.float32), _ptr(al, torch.float32),
@@ -224,9 +229,10 @@ def sd_markov_draft_workspace_size(R, gamma, V, rank):
 
 
 def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, workspace=None,
-                    out=None, stream=None):
+                    out=None, stream=None, stats=False):
     """Run the Markov drafting head.  Returns a dict of device tensors:
-    tokens [R][gamma], q_logits [R][gamma][V] bf16, conf [R][gamma], status [R]."""
+    tokens [R][gamma], q_logits [R][gamma][V] bf16, conf [R][gamma], status [R],
+    and q_stats [R][gamma][2] ((m, Z) of each drafted row) if stats."""
     R, gamma, V = U.shape
     rank = A.shape[2]
     H = h.shape[2]
@@ -238,16 +244,18 @@ def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, w
     ql = o.get("q_logits", torch.empty((R, gamma, V), dtype=bf, device=dev))
     conf = o.get("conf", torch.empty((R, gamma), dtype=torch.float32, device=dev))
     status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
+    qs = o.get("q_stats", torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
     wsz = sd_markov_draft_workspace_size(R, gamma, V, rank)
     ws = workspace if workspace is not None else _workspace(wsz, dev)
     code = lib().sd_markov_draft(
         _stream(stream), R, gamma, V, rank, float(temperature), int(seed) & (2**64 - 1),
         _ptr(pos0, torch.int64, "pos0"), _ptr(U, bf, "U"), _ptr(A, bf, "A"), _ptr(Ct, bf, "Ct"),
         _ptr(x0, torch.int32, "x0"), _ptr(h, bf, "h"), H, _ptr(E, bf, "E"), rank_e,
-        _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf), _ptr(conf, torch.float32),
-        _ptr(status, torch.int32), ws.data_ptr(), ws.numel())
+        _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf),
+        _ptr(qs, torch.float32, "q_stats"), _ptr(conf, torch.float32), _ptr(status, torch.int32),
+        ws.data_ptr(), ws.numel())
     _check("sd_markov_draft", code)
-    return dict(tokens=tokens, q_logits=ql, conf=conf, status=status)
+    return dict(tokens=tokens, q_logits=ql, conf=conf, status=status, q_stats=qs)
 
 
 def sd_rnn_draft_workspace_size(R, gamma, V, d):
@@ -255,9 +263,10 @@ def sd_rnn_draft_workspace_size(R, gamma, V, d):
 
 
 def sd_rnn_draft(U, W, Es, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, workspace=None,
-                 out=None, stream=None):
+                 out=None, stream=None, stats=False):
     """Run the RNN drafting head.  Returns a dict of device tensors:
-    tokens [R][gamma], q_logits [R][gamma][V] bf16, conf [R][gamma], status [R]."""
+    tokens [R][gamma], q_logits [R][gamma][V] bf16, conf [R][gamma], status [R],
+    and q_stats [R][gamma][2] ((m, Z) of each drafted row) if stats."""
     R, gamma, V = U.shape
     d = W.shape[0]
     H = h.shape[2]
@@ -269,16 +278,18 @@ def sd_rnn_draft(U, W, Es, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, 
     ql = o.get("q_logits", torch.empty((R, gamma, V), dtype=bf, device=dev))
     conf = o.get("conf", torch.empty((R, gamma), dtype=torch.float32, device=dev))
     status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
+    qs = o.get("q_stats", torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
     ws = workspace if workspace is not None else _workspace(sd_rnn_draft_workspace_size(R, gamma, V, d),
                                                             dev)
     code = lib().sd_rnn_draft(
         _stream(stream), R, gamma, V, d, float(temperature), int(seed) & (2**64 - 1),
         _ptr(pos0, torch.int64, "pos0"), _ptr(U, bf, "U"), _ptr(W, bf, "W"), _ptr(Es, bf, "Es"),
         _ptr(Ct, bf, "Ct"), _ptr(x0, torch.int32, "x0"), _ptr(h, bf, "h"), H, _ptr(E, bf, "E"), rank_e,
-        _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf), _ptr(conf, torch.float32),
-        _ptr(status, torch.int32), ws.data_ptr(), ws.numel())
+        _ptr(w, torch.float32, "w"), _ptr(tokens, torch.int32), _ptr(ql, bf),
+        _ptr(qs, torch.float32, "q_stats"), _ptr(conf, torch.float32), _ptr(status, torch.int32),
+        ws.data_ptr(), ws.numel())
     _check("sd_rnn_draft", code)
-    return dict(tokens=tokens, q_logits=ql, conf=conf, status=status)
+    return dict(tokens=tokens, q_logits=ql, conf=conf, status=status, q_stats=qs)
 
 
 def sd_stream_read(src, sink=None, stream=None):

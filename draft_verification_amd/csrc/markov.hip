@@ -18,7 +18,8 @@
 //                    the first stage loads
 //   k_markov_select  one workgroup per request: confidence of position k,
 //                    combine tile partials, locate the inverse-CDF tile,
-//                    rescan 128 logits, emit x_k
+//                    rescan 128 logits, emit x_k (and, when asked, the row's
+//                    (m, Z), which spares the verifier a pass over the row)
 // plus, up front, one k_hidden_dot launch for w_h . h_k of every position.
 #include <algorithm>
 
@@ -355,12 +356,12 @@ __device__ void rnn_next_state(const NextRows& nr, int r, int V, int tok, float 
 // computed while the tile's logits are in flight.
 template <bool RNN>
 __global__ __launch_bounds__(kThreads) void k_markov_select(
-    int gamma, int k, int V, int H, int rank_e, float c, uint64_t seed,
+    int gamma, int k, int V, int H, int rank_e, float c, float inv_t, uint64_t seed,
     const int64_t* __restrict__ pos0, const int32_t* __restrict__ x0,
     const uint16_t* __restrict__ E, const float* __restrict__ w,
     const float* __restrict__ hdot, const float2* __restrict__ partial, int n_tiles,
     const uint16_t* __restrict__ q_logits, NextRows nr, int32_t* __restrict__ tokens,
-    float* __restrict__ conf, int32_t* __restrict__ status) {
+    float2* __restrict__ q_stats, float* __restrict__ conf, int32_t* __restrict__ status) {
   __shared__ float s_s[kMaxRank];
   __shared__ float s_red[kThreads / 64];
   __shared__ float s_rede[kThreads / 64];
@@ -424,6 +425,8 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   int bad = 0;
   if (isnan(M) || isnan(Z) || M == __builtin_huge_valf()) bad = SD_ST_NONFINITE;
   else if (M == kNegInf) bad = SD_ST_ZERO_Z;
+  // the row's normaliser, for the verifier
+  if (q_stats && tid == 0) q_stats[(size_t)r * gamma + (k - 1)] = sdv::stats_report(M, REF, Z, inv_t);
   const int64_t pbase = pos0 ? pos0[r] : 0;
   const double u = sdv::uniform24(seed, (uint64_t)r, (uint64_t)(pbase + k), 0);
   const double target = u * Z;
@@ -577,11 +580,12 @@ int check_head_args(int R, int gamma, int V, int H, int rank_e, float temperatur
 // The sequential loop shared by both heads: per step the bias GEMM + epilogue,
 // then the select kernel (which also prepares the next step's rows).
 template <int NSPLIT>
-int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_stride, float c,
-             uint64_t seed, const int64_t* pos0, const uint16_t* U, const uint16_t* A, const uint16_t* Ct,
-             const int32_t* x0, int H, const uint16_t* E, int rank_e, const float* w,
-             const float* hdot, float2* partial, const NextRows& nr, int32_t* tokens,
-             uint16_t* q_logits, float* conf, int32_t* status) {
+int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_stride,
+             float temperature, uint64_t seed, const int64_t* pos0, const uint16_t* U,
+             const uint16_t* A, const uint16_t* Ct, const int32_t* x0, int H, const uint16_t* E,
+             int rank_e, const float* w, const float* hdot, float2* partial, const NextRows& nr,
+             int32_t* tokens, uint16_t* q_logits, float* q_stats, float* conf, int32_t* status) {
+  const float c = sdv::kLog2e / temperature, inv_t = 1.0f / temperature;
   const int n_tiles = (V + kTileN - 1) / kTileN;
   int dev = 0, n_cu = 0;
   SDV_TRY_LAUNCH(hipGetDevice(&dev));
@@ -594,9 +598,9 @@ int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_st
                                gamma, k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag, A, x0,
                                (const int32_t*)tokens, q_logits, partial, n_tiles));
     SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT == 2>, dim3(R), dim3(kThreads), 0, stream, gamma,
-                               k, V, H, rank_e, c, seed, pos0, x0, E, w, hdot,
+                               k, V, H, rank_e, c, inv_t, seed, pos0, x0, E, w, hdot,
                                (const float2*)partial, n_tiles, (const uint16_t*)q_logits, nr, tokens,
-                               conf, status));
+                               (float2*)q_stats, conf, status));
   }
   return SD_OK;
 }
@@ -613,7 +617,7 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
                                const uint16_t* U, const uint16_t* A, const uint16_t* Ct,
                                const int32_t* x0, const uint16_t* h, int H, const uint16_t* E,
                                int rank_e, const float* w, int32_t* tokens, uint16_t* q_logits,
-                               float* conf, int32_t* status, void* workspace,
+                               float* q_stats, float* conf, int32_t* status, void* workspace,
                                size_t workspace_bytes) {
   const int rc = check_head_args(R, gamma, V, H, rank_e, temperature);
   if (rc != SD_OK) return rc;
@@ -626,7 +630,7 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
   if (!workspace || workspace_bytes < markov_ws_bytes(R, gamma, V, rank)) return SD_ERANGE;
   if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
   if ((((uintptr_t)U | (uintptr_t)A | (uintptr_t)Ct | (uintptr_t)q_logits | (uintptr_t)h |
-        (uintptr_t)w) & 15) != 0)
+        (uintptr_t)w) & 15) != 0 || ((uintptr_t)q_stats & 7) != 0)
     return SD_EINVAL;
 
   const int n_tiles = (V + kTileN - 1) / kTileN;
@@ -640,9 +644,8 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
   const int rows = R * gamma;
   SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
                              rows, hdot));
-  return run_head<1>(stream, R, gamma, V, rank, (size_t)V * rank, sdv::kLog2e / temperature, seed,
-                     pos0, U, A, Ct, x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf,
-                     status);
+  return run_head<1>(stream, R, gamma, V, rank, (size_t)V * rank, temperature, seed, pos0, U, A, Ct,
+                     x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, q_stats, conf, status);
 }
 
 extern "C" size_t sd_rnn_draft_workspace_size(int R, int gamma, int V, int d) {
@@ -655,7 +658,7 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
                             const uint16_t* W, const uint16_t* Es, const uint16_t* Ct,
                             const int32_t* x0, const uint16_t* h, int H, const uint16_t* E,
                             int rank_e, const float* w, int32_t* tokens, uint16_t* q_logits,
-                            float* conf, int32_t* status, void* workspace,
+                            float* q_stats, float* conf, int32_t* status, void* workspace,
                             size_t workspace_bytes) {
   const int rc = check_head_args(R, gamma, V, H, rank_e, temperature);
   if (rc != SD_OK) return rc;
@@ -669,7 +672,7 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
   if (!workspace || workspace_bytes < rnn_ws_bytes(R, gamma, V, d)) return SD_ERANGE;
   if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
   if ((((uintptr_t)U | (uintptr_t)W | (uintptr_t)Ct | (uintptr_t)q_logits | (uintptr_t)h |
-        (uintptr_t)w) & 15) != 0)
+        (uintptr_t)w) & 15) != 0 || ((uintptr_t)q_stats & 7) != 0)
     return SD_EINVAL;
 
   const int n_tiles = (V + kTileN - 1) / kTileN;
@@ -687,6 +690,6 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
                              rows, hdot));
   SDV_TRY_LAUNCH(sdv::launch(k_rnn_init, dim3(R), dim3(kThreads), 0, stream, R, V, d, Es, x0, nr.state,
                              nr.Ag));
-  return run_head<2>(stream, R, gamma, V, d, 0, sdv::kLog2e / temperature, seed, pos0, U, nullptr, Ct,
-                     x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, conf, status);
+  return run_head<2>(stream, R, gamma, V, d, 0, temperature, seed, pos0, U, nullptr, Ct, x0, H, E,
+                     rank_e, w, hdot, partial, nr, tokens, q_logits, q_stats, conf, status);
 }

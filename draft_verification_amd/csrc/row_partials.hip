@@ -9,7 +9,8 @@
 // issues all of its 16-byte non-temporal loads together, takes the max and
 // then sum 2^(x*c - fp32(max*c)) in registers, and each wave leaves one
 // partial (max, sum).  No LDS, no barrier.  Workgroups of rows outside the
-// scheduled batch exit at once.
+// scheduled batch exit at once.  When the drafter hands over its rows'
+// statistics the pass covers the target rows alone.
 #include "sdv_host.h"
 #include "verify_common.h"
 
@@ -25,10 +26,10 @@ __global__ __launch_bounds__(kRowThreads) void k_row_partials(sdv::RowPassArgs a
   using VT = sdv::Vec<BF16>;
   constexpr int kVec = kChunk / VT::kElems / kRowThreads;
   const int item = blockIdx.x;
-  const int S = 2 * a.gmax + 1;
   const int ch = item % a.n_ch;
-  const int rs = item / a.n_ch;
-  const int slot = rs % S, r = rs / S;
+  const int rl = item / a.n_ch;
+  const int slot = rl % a.slots, r = rl / a.slots;
+  const int rs = r * (2 * a.gmax + 1) + slot;  // row of the partials' layout
   const int L = sdv::clampi(a.ell[r], 0, a.gmax);
   if (!sdv::slot_in_batch(slot, a.gmax, L)) return;
   const char* row = slot <= a.gmax

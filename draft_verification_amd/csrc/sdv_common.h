@@ -91,6 +91,35 @@ SDV_DEV void st_nt(void* p, uint4 v) {
 
 SDV_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// ---------------------------------------------------------------------------
+// Row statistics across the library's boundary: (m, Z) with m = max(row)/T
+// and Z = sum exp(row/T - m).  Inside the kernels a row is held as (ref, Zi):
+// ref = fp32(max * c) with c = log2(e)/T, Zi = sum 2^(x*c - ref).  Z is taken
+// relative to the reported (rounded) m, so that reading a reported pair back
+// gives the frame it came from, to within the fp32 rounding of Z.
+constexpr double kLog2eD = 1.4426950408889634074;
+
+SDV_DEV float2 stats_report(float M, float ref, double Zi, float inv_t) {
+  const float m = M * inv_t;
+  if (M == -__builtin_huge_valf()) return make_float2(m, 0.0f);  // all -inf: (-inf, 0)
+  return make_float2(m, (float)(Zi * exp2((double)ref - (double)m * kLog2eD)));
+}
+
+// A reported pair in the kernels' frame; returns SD_ST_NONFINITE for NaN,
+// m = +inf or Z outside (0, inf), SD_ST_ZERO_Z for m = -inf, else 0.
+SDV_DEV int stats_read(float2 mz, float* ref, double* Zi) {
+  *ref = 0.0f;
+  *Zi = 0.0;
+  const float m = mz.x, Z = mz.y;
+  if (isnan(m) || isnan(Z) || m == __builtin_huge_valf()) return SD_ST_NONFINITE;
+  if (m == -__builtin_huge_valf()) return SD_ST_ZERO_Z;
+  if (!(Z > 0.0f) || Z == __builtin_huge_valf()) return SD_ST_NONFINITE;
+  const double e = (double)m * kLog2eD;
+  *ref = (float)e;
+  *Zi = (double)Z * exp2(e - (double)*ref);
+  return 0;
+}
+
 }  // namespace sdv
 
 // Host-side helpers.

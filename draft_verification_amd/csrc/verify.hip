@@ -12,7 +12,8 @@
 // Kernels (one stream, no host synchronisation):
 //   k_row_partials  (row_partials.hip) the bandwidth pass: one partial
 //                   (max, sum 2^(x*c - ref)) per wave and 16384-element chunk
-//                   of every batch row
+//                   of every batch row (of every target row when the drafter
+//                   supplied its rows' (m, Z): it normalised q when it drew)
 //   k_finish        one 1024-thread workgroup per request does the rest:
 //                   combine the partials into (m, Z) per row, run every accept
 //                   test at once, find the first rejection, write the accepted
@@ -55,6 +56,7 @@ struct VerifyArgs {
   const int32_t* tgt_row0;
   const char* drf;
   const int32_t* drf_row0;
+  const float2* drf_stats;  // [R][gmax] (m, Z) of the draft rows, or null
   const int32_t* draft_tokens;
   const int32_t* ell;
   const int64_t* pos0;
@@ -172,7 +174,6 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   using VT = sdv::Vec<BF16>;
   constexpr int VL = kBlk / VT::kElems / 64;  // vectors per lane per row of a block
   constexpr int kBlkVec = kBlk / VT::kElems;
-  __shared__ float sM[kMaxSlots];
   __shared__ float sRef[kMaxSlots];
   __shared__ double sZ[kMaxSlots];
   __shared__ float2 sPart[kStagedParts];
@@ -195,13 +196,16 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   }
 
   // The accept tests' operands (thread j-1 tests position j: the drafted
-  // token and its two logits) are requested first, then the partials.
+  // token, its two logits and, when the drafter supplied it, the draft row's
+  // (m, Z)) are requested first, then the partials.
   const int32_t* drafts = a.draft_tokens + (size_t)r * gmax;
   const int jt = tid + 1;
   int xj = -1;
   float ltj = 0.0f, ldj = 0.0f;
+  float2 mzj = make_float2(0.0f, 0.0f);
   if (jt <= L) {
     xj = drafts[jt - 1];
+    if (a.drf_stats) mzj = a.drf_stats[(size_t)r * gmax + (jt - 1)];
     if (xj >= 0 && xj < V) {
       ltj = VT::at(a.tgt + ((int64_t)a.tgt_row0[r] + (jt - 1)) * a.ld_bytes, xj);
       ldj = VT::at(a.drf + ((int64_t)a.drf_row0[r] + (jt - 1)) * a.ld_bytes, xj);
@@ -209,8 +213,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   }
 
   // Stage the partials of the batch rows (target slots 0..L, then draft slots
-  // gmax+1..gmax+L, i.e. local row b) in LDS when they fit: one load each.
-  const int nrows = 2 * L + 1;
+  // gmax+1..gmax+L unless their statistics were supplied, i.e. local row b)
+  // in LDS when they fit: one load each.
+  const int nrows = a.drf_stats ? L + 1 : 2 * L + 1;
   const bool staged = (long long)nrows * nparts <= kStagedParts;
   const float2* base = a.partial + (size_t)r * S * nparts;
   if (staged) {
@@ -240,21 +245,27 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) Z += __shfl_xor(Z, o, 16);
     if (gl == 0) {
-      sM[slot] = M;
       sRef[slot] = ref;
       sZ[slot] = Z;
       a.row_ref[(size_t)r * S + slot] = ref;
       a.row_z[(size_t)r * S + slot] = Z;
       const int st = row_status(M, Z);
       if (st) atomicOr(&s_st, st);
-      if (a.row_stats) {
-        // report m = max(x)/T and Z = sum exp(x/T - m): move Z from the fp32
-        // reference to the exact one
-        const double zrep = Z * exp2((double)ref - (double)M * (double)c);
-        a.row_stats[((size_t)r * S + slot) * 2 + 0] = M * a.inv_t;
-        a.row_stats[((size_t)r * S + slot) * 2 + 1] = (float)zrep;
-      }
+      if (a.row_stats)
+        ((float2*)a.row_stats)[(size_t)r * S + slot] = sdv::stats_report(M, ref, Z, a.inv_t);
     }
+  }
+  if (a.drf_stats && jt <= L) {  // the drafter's statistics of draft row jt
+    const int slot = gmax + jt;
+    float ref;
+    double Z;
+    const int st = sdv::stats_read(mzj, &ref, &Z);
+    if (st) atomicOr(&s_st, st);
+    sRef[slot] = ref;
+    sZ[slot] = Z;
+    a.row_ref[(size_t)r * S + slot] = ref;
+    a.row_z[(size_t)r * S + slot] = Z;
+    if (a.row_stats) ((float2*)a.row_stats)[(size_t)r * S + slot] = mzj;
   }
   __syncthreads();
 
@@ -618,7 +629,7 @@ extern "C" size_t sd_verify_workspace_size(int R, int gamma_max, int V) {
 extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype,
                          float temperature, uint64_t seed, const int64_t* pos0,
                          const void* tgt_logits, const int32_t* tgt_row0, const void* drf_logits,
-                         const int32_t* drf_row0, const int32_t* draft_tokens,
+                         const int32_t* drf_row0, const float* drf_stats, const int32_t* draft_tokens,
                          const int32_t* ell, int32_t* n_accepted, int32_t* out_tokens,
                          int32_t* status, float* probe_probs, float* row_stats,
                          float* accept_prob, void* workspace, size_t workspace_bytes,
@@ -636,8 +647,10 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   if (((uintptr_t)workspace & 255) != 0) return SD_EINVAL;
   if ((((uintptr_t)tgt_logits) & 15) != 0 || (drf_logits && (((uintptr_t)drf_logits) & 15) != 0))
     return SD_EINVAL;
+  if ((((uintptr_t)drf_stats) & 7) != 0 || (((uintptr_t)row_stats) & 7) != 0) return SD_EINVAL;
   const int n_ch = (V + kChunk - 1) / kChunk;
-  const long long items = (long long)R * (2 * gamma_max + 1) * n_ch;
+  const int slots = drf_stats ? gamma_max + 1 : 2 * gamma_max + 1;  // rows the bandwidth pass reads
+  const long long items = (long long)R * slots * n_ch;
   if (items > 0xFFFFFFFFLL / sdv::kRowThreads) return SD_EUNSUPPORTED;  // work-items of one launch
   const int64_t ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
   const float c = sdv::kLog2e / temperature;
@@ -661,12 +674,14 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   ra.gmax = gamma_max;
   ra.V = V;
   ra.n_ch = n_ch;
+  ra.slots = slots;
 
   VerifyArgs a;
   a.tgt = (const char*)tgt_logits;
   a.tgt_row0 = tgt_row0;
   a.drf = drf;
   a.drf_row0 = drf_row0;
+  a.drf_stats = (const float2*)drf_stats;
   a.draft_tokens = draft_tokens;
   a.ell = ell;
   a.pos0 = pos0;

@@ -64,9 +64,12 @@ struct RowPassArgs {
   int gmax;
   int V;
   int n_ch;
+  int slots;        // leading slots of each request the pass covers: 2*gmax+1,
+                    // or gmax+1 (target rows only) when the drafter's
+                    // statistics replace the draft rows
 };
 
-// Launch the bandwidth pass over items = R * (2*gmax+1) * n_ch workgroups.
+// Launch the bandwidth pass over items = R * slots * n_ch workgroups.
 hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned items, hipStream_t stream);
 
 }  // namespace sdv

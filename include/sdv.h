@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 2
+#define SDV_ABI_VERSION 3
 
 /* return codes (host side) */
 #define SD_OK             0
@@ -168,6 +168,17 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *   pos0        [R] int64 or NULL (all 0)
  *   tgt_logits, drf_logits   row-major logit rows (dtype), see above
  *   tgt_row0, drf_row0       [R] int32 first row of each request
+ *   drf_stats    [R][gamma_max][2] fp32 or NULL: (m, Z) of the draft row of
+ *                each position j = 1..gamma_max, in row_stats' format below.
+ *                The drafter normalised q_j when it sampled x_j, so it can
+ *                hand the normaliser over (sd_markov_draft and sd_rnn_draft
+ *                write it as q_stats, at their own temperature, which must be
+ *                T).  When given, the draft rows are not streamed: only
+ *                q_j(x_j) and the rejected row are read, and the row pass
+ *                covers the 1 + ell target rows of each request alone.  A
+ *                pair with m = -inf is an all -inf row (ZERO_Z); NaN, m =
+ *                +inf, or Z not in (0, inf) marks it NONFINITE.  8-byte
+ *                aligned.
  *   draft_tokens [R][gamma_max] int32
  *   ell          [R] int32 verified lengths, clamped to [0, gamma_max]
  *                (typically sd_schedule's output, never read on the host)
@@ -181,6 +192,8 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *               Z = sum exp(row/T - m): slots 0..gamma_max are target rows of
  *               positions 1..gamma_max+1, slots gamma_max+1.. are draft rows of
  *               positions 1..gamma_max; only slots inside the batch are written
+ *               (draft slots copy drf_stats when it is given).  An all -inf
+ *               row reports (-inf, 0).
  *   accept_prob [R][gamma_max] fp32 or NULL: alpha_j = sum_v min(p_j(v), q_j(v)),
  *               the probability that position j is accepted given the prefix
  *               was, i.e. 1 - TV(p_j, q_j), the label the confidence head is
@@ -201,7 +214,7 @@ size_t sd_verify_workspace_size(int R, int gamma_max, int V);
 int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype,
               float temperature, uint64_t seed, const int64_t* pos0,
               const void* tgt_logits, const int32_t* tgt_row0,
-              const void* drf_logits, const int32_t* drf_row0,
+              const void* drf_logits, const int32_t* drf_row0, const float* drf_stats,
               const int32_t* draft_tokens, const int32_t* ell,
               int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
               float* probe_probs, float* row_stats, float* accept_prob,
@@ -232,7 +245,11 @@ int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype
  *   h        [R][gamma][H] bf16 backbone hidden states
  *   E        [V][rank_e] bf16 Markov embedding;  w [H + rank_e] fp32
  * Outputs: tokens [R][gamma] int32, q_logits [R][gamma][V] bf16,
- *   conf [R][gamma] fp32, status [R] int32.
+ *   conf [R][gamma] fp32, status [R] int32, and q_stats [R][gamma][2] fp32
+ *   or NULL: (m, Z) of each row L_k[r] with m = max(L_k[r])/T and
+ *   Z = sum exp(L_k[r]/T - m) (sd_verify's row_stats format; (-inf, 0) for
+ *   an all -inf row), the normaliser the draw used, for sd_verify's
+ *   drf_stats.
  * Degenerate data: an anchor outside [0, V) sets BAD_TOKEN and contributes
  * neither bias nor embedding; a row of L_k with NaN / +inf (NONFINITE) or all
  * -inf (ZERO_Z) yields token -1 at that position (and BAD_TOKEN next).
@@ -243,8 +260,8 @@ int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
                     const uint16_t* U, const uint16_t* A, const uint16_t* Ct,
                     const int32_t* x0, const uint16_t* h, int H,
                     const uint16_t* E, int rank_e, const float* w,
-                    int32_t* tokens, uint16_t* q_logits, float* conf, int32_t* status,
-                    void* workspace, size_t workspace_bytes);
+                    int32_t* tokens, uint16_t* q_logits, float* q_stats, float* conf,
+                    int32_t* status, void* workspace, size_t workspace_bytes);
 
 /*
  * sd_rnn_draft - the RNN form of the sequential head [DS innovation one]:
@@ -268,8 +285,8 @@ int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, float tempe
                  uint64_t seed, const int64_t* pos0, const uint16_t* U, const uint16_t* W,
                  const uint16_t* Es, const uint16_t* Ct, const int32_t* x0, const uint16_t* h,
                  int H, const uint16_t* E, int rank_e, const float* w, int32_t* tokens,
-                 uint16_t* q_logits, float* conf, int32_t* status, void* workspace,
-                 size_t workspace_bytes);
+                 uint16_t* q_logits, float* q_stats, float* conf, int32_t* status,
+                 void* workspace, size_t workspace_bytes);
 
 /*
  * Training-free two-stage budget planner [LS: two optimisation stages, EMA

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sdv.sd_abi_version() == 2
+    assert sdv.sd_abi_version() == 3
     assert sdv.sd_status_string(0) == "ok"
     for code in (-1, -2, -3, -4, 1, 2, 4, 8, 16):
         assert sdv.sd_status_string(code) != "unknown status"
@@ -65,12 +65,13 @@ def test_schedule_host_validation():
     assert _sched(4, 4, 0, 20, ws=64) == _lib.SD_ERANGE          # workspace < 16 keys
 
 
-def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=()):
+def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=(), dstats=None, rstats=None):
     L = sdv.lib()
     P = lambda name: None if name in nulls else ctypes.c_void_p(256)
+    opt = lambda a: None if a is None else ctypes.c_void_p(a)
     return L.sd_verify(None, R, g, V, ld, dt, T, 1, None, P("tgt"), P("t0"), P("drf"), P("d0"),
-                       P("toks"), P("ell"), P("nacc"), P("out"), P("st"), None, None, None,
-                       ctypes.c_void_p(ws_ptr), ws, None, None)
+                       opt(dstats), P("toks"), P("ell"), P("nacc"), P("out"), P("st"), None,
+                       opt(rstats), None, ctypes.c_void_p(ws_ptr), ws, None, None)
 
 
 def test_verify_host_validation():
@@ -86,15 +87,18 @@ def test_verify_host_validation():
     assert _ver(nulls=("tgt",)) == _lib.SD_EINVAL
     assert _ver(nulls=("ell",)) == _lib.SD_EINVAL
     assert _ver(R=0) == _lib.SD_OK                                  # nothing to do
+    assert _ver(dstats=260) == _lib.SD_EINVAL                       # (m, Z) pairs need 8 bytes
+    assert _ver(rstats=260) == _lib.SD_EINVAL
     # 1024 requests x 511 rows x 64 chunks: more work-items than one launch holds
     assert _ver(R=1024, g=255, V=1 << 20, ld=1 << 20, ws=1 << 40) == _lib.SD_EUNSUPPORTED
 
 
-def _mk(R=2, g=2, V=64, rank=32, H=8, re_=8, T=1.0, ws=1 << 20, nulls=()):
+def _mk(R=2, g=2, V=64, rank=32, H=8, re_=8, T=1.0, ws=1 << 20, nulls=(), qstats=None):
     L = sdv.lib()
     P = lambda name: None if name in nulls else ctypes.c_void_p(256)
+    qs = None if qstats is None else ctypes.c_void_p(qstats)
     return L.sd_markov_draft(None, R, g, V, rank, T, 1, None, P("U"), P("A"), P("C"), P("x0"),
-                             P("h"), H, P("E"), re_, P("w"), P("tok"), P("ql"), P("conf"),
+                             P("h"), H, P("E"), re_, P("w"), P("tok"), P("ql"), qs, P("conf"),
                              P("st"), ctypes.c_void_p(256), ws)
 
 
@@ -107,6 +111,7 @@ def test_markov_host_validation():
     assert _mk(ws=8) == _lib.SD_ERANGE
     assert _mk(nulls=("C",)) == _lib.SD_EINVAL
     assert _mk(R=0) == _lib.SD_OK
+    assert _mk(qstats=260) == _lib.SD_EINVAL                        # (m, Z) pairs need 8 bytes
 
 
 def test_stream_read_host_validation():

@@ -1,11 +1,14 @@
-"""GPU parity of sd_markov_draft against the oracle, with teacher forcing.
+"""GPU parity of sd_markov_draft against the oracle.
 
-For every checked (request, position) the oracle is given the GPU's previous
-token and computes the exact pre-rounding logits y = U + A_k[x] . C_k (fp64):
-the GPU's bf16 logits must be a round-to-nearest of some value within
-1e-5 * sum|A_k[x]_i C_k[i, v]| (+ fp32 rounding of the add) of y.  The token
-is then re-drawn by the oracle from the GPU's rounded logits and must match
-unless near-boundary; the confidence must match within 1e-5 relative.
+The oracle runs its own sequential chain from the same seeded inputs; no GPU
+output enters it.  Request by request, while the two chains share their
+drafted history: each GPU bf16 logit must be a round-to-nearest of a value
+within 1e-5 * sum|A_k[x]_i C_k[i, v]| (+ 1e-7 |y|, the fp32 add) of the
+oracle's exact y = U + A_k[x] . C_k (fp64); the confidence and the row's
+(m, Z) must match within 1e-5 relative; the tokens must be equal, except
+where the oracle's draw is near-boundary (distance below 1e-6), where the
+chains may part — what follows a parting is drawn from another history and
+is not compared.
 """
 
 import numpy as np
@@ -15,65 +18,89 @@ import torch
 import draft_verification_amd as sdv
 from oracle import markov as OM
 from oracle import schedule as OS
+from oracle import verify as OV
 from workloads import markov_inputs, markov_config, markov_targets
-from tests.parity_util import (to_np, oracle_verify_subset, compare_verify, check_stats, NEAR,
-                               assert_rel)
+from tests.parity_util import (to_np, compare_verify, check_stats, compare_draft_chains,
+                               bf16_half_ulp, partings_bound, check_drafted_row_stats, cdf_shift)
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp):
+def _run(inp, stats=True):
     out = sdv.sd_markov_draft(inp["U"], inp["A"], inp["Ct"], inp["x0"], inp["h"], inp["E"], inp["w"],
-                              inp["temperature"], inp["seed"], pos0=inp.get("pos0"))
+                              inp["temperature"], inp["seed"], pos0=inp.get("pos0"), stats=stats)
     torch.cuda.synchronize()
     return out
 
 
-def _bf16_half_ulp(y):
-    _, e = np.frexp(y)
-    e = np.maximum(e, -125)
-    return np.ldexp(0.5, e - 8)
+def _f(t):
+    return to_np(t).astype(np.float64)
 
 
-def _teacher_forced_check(inp, out, reqs):
-    T, seed = inp["temperature"], inp["seed"]
-    toks = to_np(out["tokens"])
-    conf = to_np(out["conf"])
-    ql = out["q_logits"]
-    x0 = to_np(inp["x0"])
-    gamma = inp["gamma"]
-    H = inp["H"]
-    near = 0
-    mism = 0
-    w = to_np(inp["w"]).astype(np.float64)
-    E = inp["E"]
+def oracle_chain(inp, reqs, keep=()):
+    """The oracle's Markov chain for requests `reqs`, from the seeded inputs
+    alone (the tables A_k, C_k converted once per position).  For the
+    requests in `keep` it also keeps, per position, the exact logits y, the
+    rounded L and the logits' tolerance."""
+    T, seed, V, gamma = inp["temperature"], inp["seed"], inp["V"], inp["gamma"]
+    reqs = [int(r) for r in reqs]
+    n = len(reqs)
+    idx = torch.as_tensor(reqs, dtype=torch.long, device=inp["U"].device)
+    U = inp["U"].index_select(0, idx)
+    h = inp["h"].index_select(0, idx)
+    x_prev = to_np(inp["x0"])[reqs].astype(np.int64)
+    pos0 = (np.zeros(n, np.int64) if inp.get("pos0") is None
+            else to_np(inp["pos0"])[reqs].astype(np.int64))
+    E, w = _f(inp["E"]), _f(inp["w"])
+    kept = [i for i, r in enumerate(reqs) if r in set(keep)]
+    ref = dict(tokens=np.zeros((n, gamma), np.int64), conf=np.zeros((n, gamma)),
+               dists=np.zeros((n, gamma)), status=np.zeros(n, np.int32), y={}, L={}, tol={},
+               rows=np.zeros((n, gamma, V), np.float32))
     for k in range(1, gamma + 1):
-        A_k = to_np(inp["A"][k - 1]).astype(np.float64)
-        C_k = to_np(inp["Ct"][k - 1]).astype(np.float64).T
-        for r in reqs:
-            xp = int(x0[r]) if k == 1 else int(toks[r, k - 2])
-            U = to_np(inp["U"][r, k - 1]).astype(np.float64)[None]
-            h = to_np(inp["h"][r, k - 1]).astype(np.float64)[None]
-            y, L, _, c, st, _ = OM.markov_step(U, A_k, C_k, [xp], h, to_np(E).astype(np.float64),
-                                               w, T, seed, [r], [k])
-            Lg = to_np(ql[r, k - 1]).astype(np.float64)
-            if 0 <= xp < inp["V"]:
-                terms = np.abs(A_k[xp]) @ np.abs(C_k)
-            else:
-                terms = np.zeros(inp["V"])
-            tol = _bf16_half_ulp(y[0]) + 1e-5 * terms + 1e-7 * np.abs(y[0]) + 1e-30
-            bad = np.abs(Lg - y[0]) > tol
-            assert not np.any(bad), f"r{r} k{k}: {bad.sum()} logits off; worst idx {np.argmax(np.abs(Lg - y[0]) - tol)}"
-            assert_rel(conf[r, k - 1], c[0], what=f"conf r{r} k{k}")
-            # re-draw from the GPU's rounded logits with the oracle's sampler
-            _, _, tok, _, _, dist = OM.markov_step(Lg[None], A_k, np.zeros_like(C_k), [xp], h,
-                                                   to_np(E).astype(np.float64), w, T, seed, [r], [k])
-            if toks[r, k - 1] != tok[0]:
-                assert dist[0] < NEAR, f"r{r} k{k}: gpu token {toks[r, k-1]} vs oracle {tok[0]}"
-                mism += 1
-            if dist[0] < NEAR:
-                near += 1
-    return near, mism
+        A_k = _f(inp["A"][k - 1])
+        C_k = _f(inp["Ct"][k - 1]).T
+        y, L, tok, c, st, d = OM.markov_step(_f(U[:, k - 1]), A_k, C_k, x_prev, _f(h[:, k - 1]), E, w,
+                                             T, seed, reqs, pos0 + k)
+        if kept:
+            absC = np.abs(C_k)
+        for i in kept:
+            xp = x_prev[i]
+            terms = np.abs(A_k[xp]) @ absC if 0 <= xp < V else np.zeros(V)
+            ref["y"][i, k - 1] = y[i]
+            ref["L"][i, k - 1] = L[i]
+            ref["tol"][i, k - 1] = bf16_half_ulp(y[i]) + 1e-5 * terms + 1e-7 * np.abs(y[i]) + 1e-30
+        ref["rows"][:, k - 1] = L   # bf16 values, exact in fp32
+        ref["tokens"][:, k - 1] = tok
+        ref["conf"][:, k - 1] = c
+        ref["dists"][:, k - 1] = d
+        ref["status"] |= st
+        x_prev = tok
+    return ref
+
+
+def check_chain(inp, out, ref, reqs):
+    """Compare along the shared history; logits and (m, Z) where kept."""
+    T, V = inp["temperature"], inp["V"]
+    ql = out["q_logits"]
+    qs = to_np(out["q_stats"]) if out.get("q_stats") is not None else None
+
+    def check_logits(i, r, k):
+        if (i, k) not in ref["y"]:
+            return
+        Lg = _f(ql[r, k])
+        bad = np.abs(Lg - ref["y"][i, k]) > ref["tol"][i, k]
+        assert not np.any(bad), (f"r{r} k{k + 1}: {bad.sum()} logits off; worst idx "
+                                 f"{np.argmax(np.abs(Lg - ref['y'][i, k]) - ref['tol'][i, k])}")
+        if qs is not None:
+            check_drafted_row_stats(qs[r, k], Lg, ref["L"][i, k], V, T, what=f"q_stats r{r} k{k + 1}")
+
+    def shift(i, r, k):
+        return cdf_shift(_f(out["q_logits"][r, k]), ref["rows"][i, k], V, T)
+
+    near, parted, compared, gone = compare_draft_chains(to_np(out["tokens"]), to_np(out["conf"]), ref,
+                                                        reqs, check_logits, shift)
+    print(f"positions compared={compared} near-boundary draws={near} chains parted={parted}")
+    return compared, parted, gone
 
 
 def test_markov_small_full():
@@ -81,25 +108,27 @@ def test_markov_small_full():
                         sigma_f=0.3, seed=91, device="cuda")
     out = _run(inp)
     assert np.all(to_np(out["status"]) == 0)
-    near, mism = _teacher_forced_check(inp, out, range(5))
-    print(f"near-boundary draws={near} diverged={mism}")
-    assert mism <= 1
+    ref = oracle_chain(inp, range(5), keep=range(5))
+    compared, parted, _ = check_chain(inp, out, ref, range(5))
+    assert parted <= partings_bound(compared)
 
 
-def test_markov_untied_run_matches_oracle_chain():
-    """Without teacher forcing: the oracle's own sequential chain reproduces
-    the GPU's tokens unless a near-boundary draw diverged."""
+def test_markov_whole_block_matches_the_oracle_draft():
+    """The oracle's whole-block entry point (markov_draft) on the same inputs:
+    tokens equal up to a near-boundary parting, statuses equal."""
     inp = markov_inputs(R=6, gamma=5, V=1000, rank=32, H=16, rank_e=8, sigma_u=1.5,
                         sigma_f=0.5, seed=92, device="cuda")
     out = _run(inp)
-    f = lambda t: to_np(t).astype(np.float64)
-    ref = OM.markov_draft(f(inp["U"]), f(inp["A"]), f(inp["Ct"]).transpose(0, 2, 1), to_np(inp["x0"]),
-                          f(inp["h"]), f(inp["E"]), f(inp["w"]), 1.0, inp["seed"])
-    toks = to_np(out["tokens"])
+    ref = OM.markov_draft(_f(inp["U"]), _f(inp["A"]), _f(inp["Ct"]).transpose(0, 2, 1), to_np(inp["x0"]),
+                          _f(inp["h"]), _f(inp["E"]), _f(inp["w"]), 1.0, inp["seed"])
+    _, parted, compared, gone = compare_draft_chains(
+        to_np(out["tokens"]), to_np(out["conf"]), ref, range(6),
+        shift=lambda i, r, k: cdf_shift(_f(out["q_logits"][r, k]), ref["L"][i, k], inp["V"], 1.0))
+    assert parted <= partings_bound(compared)
+    st = to_np(out["status"])
     for r in range(6):
-        if not np.array_equal(toks[r], ref["tokens"][r]):
-            k = int(np.argmax(toks[r] != ref["tokens"][r]))
-            assert ref["dists"][r, k] < NEAR
+        if r not in gone:
+            assert st[r] == ref["status"][r]
 
 
 def test_markov_two_row_blocks_and_pos0():
@@ -107,19 +136,9 @@ def test_markov_two_row_blocks_and_pos0():
                         sigma_f=0.4, seed=93, device="cuda")
     inp["pos0"] = torch.arange(130, dtype=torch.int64, device="cuda") * 7
     out = _run(inp)
-    # oracle positions include pos0: check by shifting pos in the teacher-forced step
-    toks = to_np(out["tokens"])
-    pos0 = to_np(inp["pos0"])
-    for r in (0, 64, 127, 128, 129):
-        for k in (1, 2):
-            xp = int(to_np(inp["x0"])[r]) if k == 1 else int(toks[r, 0])
-            A_k = to_np(inp["A"][k - 1]).astype(np.float64)
-            Lg = to_np(out["q_logits"][r, k - 1]).astype(np.float64)
-            _, _, tok, _, _, dist = OM.markov_step(
-                Lg[None], A_k, np.zeros((32, 1000)), [xp], to_np(inp["h"][r, k - 1]).astype(np.float64)[None],
-                to_np(inp["E"]).astype(np.float64), to_np(inp["w"]).astype(np.float64), 1.0,
-                inp["seed"], [r], [int(pos0[r]) + k])
-            assert toks[r, k - 1] == tok[0] or dist[0] < NEAR
+    ref = oracle_chain(inp, range(130), keep=(0, 64, 127, 128, 129))
+    compared, parted, _ = check_chain(inp, out, ref, range(130))
+    assert parted <= partings_bound(compared)
 
 
 def test_markov_degenerate_anchor_and_rows():
@@ -130,47 +149,98 @@ def test_markov_degenerate_anchor_and_rows():
     out = _run(inp)
     st = to_np(out["status"])
     toks = to_np(out["tokens"])
+    qs = to_np(out["q_stats"])
     assert st[0] == sdv.SD_ST_BAD_TOKEN
     assert st[1] & sdv.SD_ST_ZERO_Z and toks[1, 0] == -1 and st[1] & sdv.SD_ST_BAD_TOKEN
     assert st[2] & sdv.SD_ST_NONFINITE and toks[2, 1] == -1
+    assert qs[1, 0, 0] == -np.inf and qs[1, 0, 1] == 0.0     # an all -inf row reports (-inf, 0)
+    assert np.isnan(qs[2, 1, 1])                              # a NaN row: Z is NaN
+    ref = oracle_chain(inp, range(3), keep=range(3))
+    check_chain(inp, out, ref, [0])                           # no bias, no embedding: still exact
 
 
-def test_markov_draft_workload_sampled():
-    """R=128, gamma=16, V=129280, rank 256: checked on sampled requests for all
-    16 positions; then scheduled and verified end to end."""
+SAMPLED = (0, 5, 77, 127)
+
+
+@pytest.fixture(scope="module")
+def workload():
+    """R=128, gamma=16, V=129280, rank 256: the GPU's block and the oracle's
+    chain for every request (logits kept for the sampled requests)."""
     inp = markov_config(device="cuda")
     out = _run(inp)
-    assert np.all(to_np(out["status"]) == 0)
-    near, mism = _teacher_forced_check(inp, out, [0, 77, 127])
-    print(f"near-boundary draws={near} diverged={mism} of {16 * 3}")
-    assert mism <= 1
-    # confidences of every (r, k) (cheap): oracle with the GPU's previous tokens
-    toks = to_np(out["tokens"])
-    x0 = to_np(inp["x0"])
-    prev = np.concatenate([x0[:, None], toks[:, :-1]], axis=1)
-    h = to_np(inp["h"]).astype(np.float64)
-    E = to_np(inp["E"]).astype(np.float64)
-    w = to_np(inp["w"]).astype(np.float64)
-    z = h @ w[:inp["H"]] + E[prev] @ w[inp["H"]:]
-    assert_rel(to_np(out["conf"]), OM.sigmoid(z), what="conf")
+    ref = oracle_chain(inp, range(inp["R"]), keep=SAMPLED)
+    return inp, out, ref
 
-    # end to end: targets from the drafted rows, schedule, verify
+
+def test_markov_draft_workload_sampled(workload):
+    """Logits and (m, Z) on sampled requests, confidences and tokens of every
+    request along the shared histories."""
+    inp, out, ref = workload
+    assert np.all(to_np(out["status"]) == 0)
+    compared, parted, _ = check_chain(inp, out, ref, range(inp["R"]))
+    assert parted <= partings_bound(compared)
+
+
+def test_markov_schedule_and_verify_pipeline(workload):
+    """One step of the pipeline at the same sizes: schedule on the drafted
+    confidences, verify the drafted rows against target rows (seeded from the
+    backbone logits) with the head's (m, Z) handed to the verifier.  The
+    oracle runs the same pipeline from the same seeded inputs: its own chain,
+    its own schedule, its own verification.  The schedules must agree when no
+    chain parted (a parted chain drafts other confidences); verification is
+    also run on the oracle's lengths and compared on sampled requests whose
+    chains did not part."""
+    inp, out, ref = workload
     R, gamma, V = inp["R"], inp["gamma"], inp["V"]
-    tgt, sps = markov_targets(out["q_logits"])
-    vin = dict(R=R, gmax=gamma, V=V, temperature=1.0, seed=inp["seed"] + 1, pos0=None, tgt=tgt,
-               drf=out["q_logits"].view(R * gamma, V),
-               tgt_row0=torch.arange(R, dtype=torch.int32, device="cuda") * (gamma + 1),
-               drf_row0=torch.arange(R, dtype=torch.int32, device="cuda") * gamma,
-               draft_tokens=out["tokens"])
+    tgt, sps = markov_targets(inp["U"])
+    t0 = torch.arange(R, dtype=torch.int32, device="cuda") * (gamma + 1)
+    d0 = torch.arange(R, dtype=torch.int32, device="cuda") * gamma
+    drf = out["q_logits"].view(R * gamma, V)
+
+    def verify(ell_dev):
+        res = sdv.sd_verify(tgt, t0, drf, d0, out["tokens"], ell_dev, V, 1.0, inp["seed"] + 1, probe=True,
+                            stats=True, drf_stats=out["q_stats"])
+        torch.cuda.synchronize()
+        return res
+
+    # the GPU pipeline as it runs: structurally valid on every request
     sched = sdv.sd_schedule(out["conf"], sps, OS.EARLY_STOP)
-    ref_s = OS.schedule(to_np(out["conf"]), to_np(sps), OS.EARLY_STOP)
-    assert np.array_equal(to_np(sched["ell"]), ref_s["ell"])
-    gpu = sdv.sd_verify(vin["tgt"], vin["tgt_row0"], vin["drf"], vin["drf_row0"], vin["draft_tokens"],
-                        sched["ell"], V, 1.0, vin["seed"], probe=True, stats=True)
-    torch.cuda.synchronize()
-    reqs = [0, 5, 77, 127]
-    ora = oracle_verify_subset(vin, reqs, ref_s["ell"])
-    n_dec, n_near, mism = compare_verify(gpu, ora, reqs)
-    print(f"verify decisions={n_dec} near-boundary={n_near} diverged={mism}")
-    assert mism <= 1
-    check_stats(gpu, ora, reqs, ref_s["ell"], gamma)
+    run = verify(sched["ell"])
+    ell_g, n_acc, toks = to_np(sched["ell"]), to_np(run["n_acc"]), to_np(run["tokens"])
+    drafted = to_np(out["tokens"])
+    assert np.all(to_np(run["status"]) == 0)
+    for r in range(R):
+        n = n_acc[r]
+        assert 0 <= n <= ell_g[r] and np.array_equal(toks[r, :n], drafted[r, :n]) and 0 <= toks[r, n] < V
+
+    compared, parted, gone = check_chain(inp, out, ref, range(R))
+    assert parted <= partings_bound(compared)
+    ref_s = OS.schedule(ref["conf"].astype(np.float32), to_np(sps), OS.EARLY_STOP)
+    if not gone:
+        assert np.array_equal(ell_g, ref_s["ell"])
+    reqs = [r for r in SAMPLED if r not in gone]
+    assert len(reqs) >= 2
+    tgt_h = to_np(tgt.view(R, gamma + 1, V)[reqs]).astype(np.float64)
+    # the oracle's scheduled lengths, then the whole block (more accept tests)
+    for name, ell in (("scheduled", ref_s["ell"]), ("whole block", np.full(R, gamma))):
+        gpu = verify(torch.as_tensor(ell, dtype=torch.int32, device="cuda"))
+        tr0, dr0, tgt_rows, drf_rows = [], [], [], []
+        for n, r in enumerate(reqs):
+            L = int(ell[r])
+            tr0.append(len(tgt_rows))
+            tgt_rows.extend(tgt_h[n, :L + 1])
+            dr0.append(len(drf_rows))
+            drf_rows.extend(ref["rows"][r, j].astype(np.float64) for j in range(L))   # the oracle's own rows
+        ora = OV.verify(np.array(tgt_rows), np.array(tr0),
+                        np.array(drf_rows) if drf_rows else np.zeros((1, V)), np.array(dr0),
+                        ref["tokens"][reqs], ell[reqs], V, 1.0, inp["seed"] + 1, req_ids=reqs)
+        n_dec, n_near, mism = compare_verify(gpu, ora, reqs)
+        print(f"{name}: rows gpu={R + int(ell_g.sum())} oracle={ref_s['B']}; verify decisions={n_dec} "
+              f"near-boundary={n_near} diverged={mism}")
+        assert mism <= 1
+        check_stats(gpu, ora, reqs, ell, gamma, draft=False)
+        rs = to_np(gpu["row_stats"])
+        for r in reqs:   # the draft slots report the head's (m, Z) of its own rows
+            for j in range(int(ell[r])):
+                check_drafted_row_stats(rs[r, gamma + 1 + j], _f(out["q_logits"][r, j]), ref["rows"][r, j],
+                                        V, 1.0, what=f"draft row r{r} j{j + 1}")

@@ -3,6 +3,9 @@
 Accepted lengths, emitted tokens and status bits must match exactly, except
 for requests with a decision the oracle marks near-boundary (distance < 1e-6);
 (m, Z) per row and (p(x), q(x)) per tested position within 1e-5 relative.
+Where the lengths come from the scheduler, the oracle verifies with the
+oracle scheduler's lengths (checked equal to the GPU's); no GPU output is an
+oracle input.
 """
 
 import numpy as np
@@ -29,9 +32,13 @@ def _to_cuda(inp):
     return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-def _full_check(inp, ell_dev, reqs=None):
-    gpu = _gpu_verify(inp, ell_dev)
-    ell = to_np(ell_dev)
+def _full_check(inp, ell, reqs=None, ell_dev=None, **kw):
+    """ell: host lengths for the oracle (never a GPU output); ell_dev: the
+    device lengths the GPU verifies with (default: ell copied over)."""
+    ell = np.asarray(ell, np.int64)
+    if ell_dev is None:
+        ell_dev = torch.as_tensor(ell, dtype=torch.int32, device="cuda")
+    gpu = _gpu_verify(inp, ell_dev, **kw)
     R = inp["R"]
     reqs = list(range(R)) if reqs is None else list(reqs)
     ora = oracle_verify_subset(inp, reqs, ell)
@@ -48,11 +55,13 @@ def test_verify_workloads(name, mode):
     inp = _to_cuda(verify_config(name, device="cpu"))
     R, g = inp["R"], inp["gmax"]
     if mode == "full":
-        ell = torch.full((R,), g, dtype=torch.int32, device="cuda")
+        _full_check(inp, np.full(R, g))
     else:
         m = OS.EARLY_STOP if mode == "early" else OS.GLOBAL_ARGMAX
-        ell = sdv.sd_schedule(inp["conf"], inp["sps"], m)["ell"]
-    _full_check(inp, ell)
+        ell_dev = sdv.sd_schedule(inp["conf"], inp["sps"], m)["ell"]
+        ref = OS.schedule(to_np(inp["conf"]), to_np(inp["sps"]), m)
+        assert np.array_equal(to_np(ell_dev), ref["ell"])
+        _full_check(inp, ref["ell"], ell_dev=ell_dev)
 
 
 def test_verify_ragged_vocab_and_padded_rows():
@@ -60,8 +69,7 @@ def test_verify_ragged_vocab_and_padded_rows():
     for dtype in (torch.float32, torch.bfloat16):
         inp = _to_cuda(verify_inputs(R=7, gmax=5, V=40008, ld=40016, dtype=dtype, sigma_t=2.0,
                                      zipf=True, sigma_d=(0.3, 2.0), seed=77))
-        ell = torch.tensor([0, 1, 2, 3, 4, 5, 5], dtype=torch.int32, device="cuda")
-        _full_check(inp, ell)
+        _full_check(inp, [0, 1, 2, 3, 4, 5, 5])
 
 
 def test_verify_vocab_beyond_one_block_per_thread():
@@ -70,8 +78,7 @@ def test_verify_vocab_beyond_one_block_per_thread():
     for dtype in (torch.bfloat16, torch.float32):
         inp = _to_cuda(verify_inputs(R=4, gmax=2, V=1_050_632, dtype=dtype, sigma_t=2.0,
                                      zipf=True, sigma_d=(1.0, 3.0), seed=82))
-        ell = torch.tensor([2, 2, 1, 0], dtype=torch.int32, device="cuda")
-        _full_check(inp, ell)
+        _full_check(inp, [2, 2, 1, 0])
 
 
 def test_verify_without_drafts():
@@ -79,8 +86,7 @@ def test_verify_without_drafts():
     target row 0 (the bonus draw with l = 0)."""
     for dtype in (torch.bfloat16, torch.float32):
         inp = _to_cuda(verify_inputs(R=6, gmax=0, V=5000, dtype=dtype, sigma_t=2.0, zipf=True, seed=83))
-        ell = torch.zeros(6, dtype=torch.int32, device="cuda")
-        gpu, _ = _full_check(inp, ell)
+        gpu, _ = _full_check(inp, np.zeros(6))
         assert np.all(to_np(gpu["n_acc"]) == 0)
 
 
@@ -90,8 +96,7 @@ def test_verify_maximum_draft_length():
     prefixes are accepted."""
     inp = _to_cuda(verify_inputs(R=3, gmax=255, V=1024, dtype=torch.bfloat16, sigma_t=2.0,
                                  sigma_d=(0.02, 0.05), seed=84))
-    ell = torch.tensor([255, 100, 0], dtype=torch.int32, device="cuda")
-    gpu, ora = _full_check(inp, ell)
+    gpu, ora = _full_check(inp, [255, 100, 0])
     assert int(ora["n_acc"].max()) > 20          # the long chains are exercised
 
 
@@ -102,16 +107,14 @@ def test_verify_vocab_past_the_lds_block_sums():
                                  (1, 1, 1 << 24, torch.bfloat16, 86)):
         inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=dtype, sigma_t=2.0, zipf=True,
                                      sigma_d=(1.0, 3.0), seed=seed))
-        ell = torch.full((R,), g, dtype=torch.int32, device="cuda")
-        _full_check(inp, ell)
+        _full_check(inp, np.full(R, g))
 
 
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
     inp["pos0"] = torch.arange(9, dtype=torch.int64, device="cuda") * 1000 + 17
-    ell = torch.full((9,), 6, dtype=torch.int32, device="cuda")
-    _full_check(inp, ell)
+    _full_check(inp, np.full(9, 6))
 
 
 def test_verify_packed_layout():
@@ -126,7 +129,7 @@ def test_verify_packed_layout():
     inp.update(tgt=tgt.contiguous(), drf=drf.contiguous(),
                tgt_row0=torch.as_tensor(t0, dtype=torch.int32, device="cuda"),
                drf_row0=torch.as_tensor(d0, dtype=torch.int32, device="cuda"))
-    _full_check(inp, torch.as_tensor(ell_h, dtype=torch.int32, device="cuda"))
+    _full_check(inp, ell_h)
 
 
 def test_verify_headline_full_block_sampled():
@@ -136,9 +139,10 @@ def test_verify_headline_full_block_sampled():
     inp = verify_config("headline", device="cuda")
     R, g = inp["R"], inp["gmax"]
     sched = sdv.sd_schedule(inp["conf"], inp["sps"], OS.GLOBAL_ARGMAX)
-    ell = sched["ell"]
-    assert int(sched["batch"].item()) == R * (g + 1)   # the global argmax takes the full block
-    gpu, _ = _full_check(inp, ell, reqs=[0, 1, 57, 128, 200, 255])
+    ref = OS.schedule(to_np(inp["conf"]), to_np(inp["sps"]), OS.GLOBAL_ARGMAX)
+    assert np.array_equal(to_np(sched["ell"]), ref["ell"])
+    assert ref["B"] == R * (g + 1)   # the global argmax takes the full block
+    gpu, _ = _full_check(inp, ref["ell"], reqs=[0, 1, 57, 128, 200, 255], ell_dev=sched["ell"])
     n_acc = to_np(gpu["n_acc"])
     toks = to_np(gpu["tokens"])
     drafts = to_np(inp["draft_tokens"])
@@ -158,8 +162,10 @@ def test_verify_ragged_async_sampled():
     first = sdv.sd_schedule(inp["conf_prev"], inp["sps"], OS.GLOBAL_ARGMAX, gamma_r=inp["gamma_r"])
     sched = sdv.sd_schedule(inp["conf"], inp["sps"], OS.CAPPED_TOPK, gamma_r=inp["gamma_r"],
                             cap_k=first["n_sel"])
-    ell = sched["ell"]
-    gpu, _ = _full_check(inp, ell, reqs=[0, 3, 99, 256, 400, 511])
+    ref = OS.async_schedule(to_np(inp["conf"]), to_np(inp["conf_prev"]), to_np(inp["sps"]),
+                            to_np(inp["gamma_r"]))
+    assert np.array_equal(to_np(sched["ell"]), ref["ell"])
+    gpu, _ = _full_check(inp, ref["ell"], reqs=[0, 3, 99, 256, 400, 511], ell_dev=sched["ell"])
     assert np.all(to_np(gpu["status"]) == 0)   # no NaN slot was read
 
 
@@ -174,8 +180,7 @@ def test_verify_degenerate_rows_and_tokens():
     tgt[4 * 4 + 2, 0] = float("inf")                # r4: +inf in a needed row
     tgt[5 * 4 + 3, 0] = float("nan")                # r5: NaN only past l_r -> unread
     drf[6 * 3:6 * 3 + 3] = tgt[6 * 4:6 * 4 + 3]     # r6: p == q everywhere
-    ell = torch.tensor([3, 3, 3, 3, 3, 2, 3, 0], dtype=torch.int32, device="cuda")
-    gpu, ora = _full_check(inp, ell)
+    gpu, ora = _full_check(inp, [3, 3, 3, 3, 3, 2, 3, 0])
     st = to_np(gpu["status"])
     assert st[0] == sdv.SD_ST_NONFINITE and st[1] == sdv.SD_ST_ZERO_Z
     assert st[2] & sdv.SD_ST_BAD_TOKEN and st[3] & sdv.SD_ST_ZERO_Q
@@ -206,3 +211,63 @@ def test_verify_host_errors():
         sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
                       inp["draft_tokens"], ell, 64, 1.0, 1, workspace=small)
     assert e.value.code == -2
+
+
+def _draft_stats(gpu, gmax):
+    """The draft rows' (m, Z) as a call that read them reported them (row_stats
+    slots gmax+1..2*gmax): the pairs a drafter hands over."""
+    return gpu["row_stats"][:, gmax + 1:, :].contiguous()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_verify_with_draft_statistics(dtype):
+    """The drafter's (m, Z) in place of the pass over the draft rows: the
+    oracle (which reads the rows) still agrees, the target rows' statistics
+    are those of the full pass, and the supplied pairs are what row_stats
+    reports for the draft slots.  T = 0.8 and positions offset."""
+    inp = _to_cuda(verify_inputs(R=9, gmax=6, V=40008, ld=40016, dtype=dtype, sigma_t=2.0,
+                                 zipf=True, sigma_d=(0.3, 2.5), seed=88, temperature=0.8))
+    inp["pos0"] = torch.arange(9, dtype=torch.int64, device="cuda") * 13
+    g = inp["gmax"]
+    ell = np.array([6, 5, 0, 1, 6, 3, 6, 2, 4])
+    full, _ = _full_check(inp, ell)
+    ds = _draft_stats(full, g)
+    gpu, _ = _full_check(inp, ell, drf_stats=ds)
+    rs_full, rs, ds_h = to_np(full["row_stats"]), to_np(gpu["row_stats"]), to_np(ds)
+    for r, L in enumerate(ell):
+        assert np.array_equal(rs[r, :L + 1], rs_full[r, :L + 1])
+        assert np.array_equal(rs[r, g + 1:g + 1 + L], ds_h[r, :L])
+
+
+def test_verify_degenerate_draft_statistics():
+    """Pairs that encode an all -inf row or a row holding NaN fail the request
+    exactly as reading the row does; pairs outside the documented domain
+    (Z = 0, Z = inf, m = +inf) fail it as NONFINITE."""
+    V, g, R = 2048, 3, 6
+    inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=torch.float32, sigma_t=2.0, seed=89))
+    inp["drf"][0 * g + 1, :] = float("-inf")   # r0: draft row 2 all -inf
+    inp["drf"][1 * g + 0, 7] = float("nan")    # r1: NaN in draft row 1
+    ell = np.full(R, g)
+    full, _ = _full_check(inp, ell)
+    st_full = to_np(full["status"])
+    assert st_full[0] == sdv.SD_ST_ZERO_Z and st_full[1] == sdv.SD_ST_NONFINITE
+    ds = _draft_stats(full, g).clone()
+    ds[2, 0] = torch.tensor([1.0, 0.0])
+    ds[3, 1] = torch.tensor([1.0, float("inf")])
+    ds[4, 2] = torch.tensor([float("inf"), 1.0])
+    gpu, _ = _full_check(inp, ell, reqs=[0, 1, 5], drf_stats=ds)
+    st, n_acc, toks = to_np(gpu["status"]), to_np(gpu["n_acc"]), to_np(gpu["tokens"])
+    for r in (2, 3, 4):
+        assert st[r] == sdv.SD_ST_NONFINITE and n_acc[r] == 0 and np.all(toks[r] == -1)
+
+
+def test_verify_headline_with_draft_statistics_sampled():
+    """The headline block (R=256, gamma=11, V=151936 bf16) with the draft
+    rows' statistics supplied: only the 3072 target rows are streamed."""
+    inp = verify_config("headline", device="cuda")
+    R, g = inp["R"], inp["gmax"]
+    ell = np.full(R, g)
+    reqs = [0, 2, 99, 255]
+    full, _ = _full_check(inp, ell, reqs=reqs)
+    gpu, _ = _full_check(inp, ell, reqs=reqs, drf_stats=_draft_stats(full, g))
+    assert np.all(to_np(gpu["status"]) == 0)

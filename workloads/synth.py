@@ -228,17 +228,18 @@ def rnn_config(device="cpu", **over):
     return rnn_inputs(seed=BASE_SEED + seed_off, device=device, **cfg)
 
 
-def markov_targets(q_logits, seed=BASE_SEED + 40, sigma=1.5, sigma_bonus=2.0):
-    """Target rows for verifying a drafted block: the row of position k is the
-    drafted logits of position k plus N(0, 1.5^2); the bonus row is N(0, 2^2).
+def markov_targets(U, seed=BASE_SEED + 40, sigma=1.5, sigma_bonus=2.0):
+    """Target rows for verifying a drafted block, from the seeded backbone
+    logits U [R][gamma][V] (the drafted rows are U plus a small bias): the row
+    of position k is U_k plus N(0, 1.5^2); the bonus row is N(0, 2^2).
     Returns tgt [R*(gamma+1)][V] bf16 in the reserved-slot layout."""
-    R, gamma, V = q_logits.shape
-    device = q_logits.device
+    R, gamma, V = U.shape
+    device = U.device
     g = _gen(device, seed)
     tgt = torch.empty((R, gamma + 1, V), dtype=torch.bfloat16, device=device)
     for r0 in range(0, R, 16):
         r1 = min(R, r0 + 16)
-        tgt[r0:r1, :gamma] = (q_logits[r0:r1].float()
+        tgt[r0:r1, :gamma] = (U[r0:r1].float()
                               + _normal((r1 - r0, gamma, V), sigma, g, device)).to(torch.bfloat16)
         tgt[r0:r1, gamma] = _normal((r1 - r0, V), sigma_bonus, g, device).to(torch.bfloat16)
     b_sat, amp, period = MARKOV["sps"]
