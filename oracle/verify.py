@@ -36,6 +36,11 @@ Near-boundary bookkeeping: every decision records its distance to the
 threshold, |u - p/q| for an accept test and the gap between u * sum(w) and the
 nearest cumulative-sum boundary over sum(w) for a sample.
 
+verify_until_rejection() takes the positions in order and stops at the
+first rejection; it never reads a row past it (pinned against verify(): the
+same result on usable rows, and rows past the rejection replaced by NaN or
+all -inf change nothing).
+
 Pins: sum min(p, q) = 1 - TV(p, q) accept frequency, chi-square losslessness,
 E[n_acc] = sum_j prod_{i<=j} alpha_i, the special cases p = q, disjoint
 supports, one-hot q, l = 0 (tests/test_oracle_verify.py).
@@ -182,5 +187,99 @@ def verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=Non
         "tgt_stats": tgt_stats,
         "drf_stats": drf_stats,
         "alpha": alpha,
+        "decisions": decisions,
+    }
+
+
+def verify_until_rejection(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, T, seed, pos0=None,
+                           req_ids=None):
+    """Verification that examines each request's rows in position order and
+    stops at the first rejection (speculative-decoding history page, "1.1
+    mechanism": everything after the first rejection is discarded, so the
+    rows past it cannot change the outcome).
+
+    Same arguments and outputs as verify(), except: rows past the first
+    rejection are never examined, so a NaN, +inf or all -inf row there fails
+    nothing; a position fails the request only when its own target or draft
+    row is unusable (and the bonus row only when every draft was accepted);
+    probe, tgt_stats and drf_stats are filled for the rows and positions
+    examined; alpha is not computed (it needs every row).  On rows that are
+    all usable the result is exactly verify()'s.
+    """
+    R = len(ell)
+    gmax = np.asarray(draft_tokens).shape[1]
+    pos0 = np.zeros(R, np.int64) if pos0 is None else np.asarray(pos0, np.int64)
+    rid = np.arange(R) if req_ids is None else np.asarray(req_ids, np.int64)
+    n_acc = np.zeros(R, np.int32)
+    tokens = np.full((R, gmax + 1), -1, np.int32)
+    status = np.zeros(R, np.int32)
+    probe = np.zeros((R, gmax, 2))
+    tgt_stats = np.zeros((R, gmax + 1, 2))
+    drf_stats = np.zeros((R, gmax, 2))
+    decisions = []
+
+    for r in range(R):
+        L = int(ell[r])
+        st = 0
+        failed = False
+        w = None
+        for j in range(1, L + 1):
+            p, m, Z, sp = row_softmax(tgt[tgt_row0[r] + j - 1], V, T)
+            tgt_stats[r, j - 1] = (m, Z)
+            q, m, Z, sq = row_softmax(drf[drf_row0[r] + j - 1], V, T)
+            drf_stats[r, j - 1] = (m, Z)
+            if (sp | sq) & (ST_NONFINITE | ST_ZERO_Z):
+                st |= sp | sq
+                failed = True
+                break
+            x = int(draft_tokens[r][j - 1])
+            if not (0 <= x < V):
+                st |= ST_BAD_TOKEN
+                accept = False
+            else:
+                probe[r, j - 1] = (p[x], q[x])
+                u = uniform(seed, int(rid[r]), int(pos0[r]) + j, DRAW_ACCEPT)
+                if q[x] == 0.0:
+                    st |= ST_ZERO_Q
+                    accept = p[x] > 0.0
+                    dist = np.inf
+                else:
+                    accept = u * q[x] < p[x]
+                    dist = abs(u - p[x] / q[x])
+                decisions.append(("accept", r, j, dist))
+            if not accept:
+                w = np.maximum(0.0, p - q)
+                if not (w.sum() > 0.0):
+                    st |= ST_ZERO_RESIDUAL
+                    w = p
+                n, pos = j - 1, j
+                break
+        if failed:
+            status[r] = st
+            continue
+        if w is None:  # every draft accepted: the bonus row
+            p, m, Z, sp = row_softmax(tgt[tgt_row0[r] + L], V, T)
+            tgt_stats[r, L] = (m, Z)
+            if sp & (ST_NONFINITE | ST_ZERO_Z):
+                status[r] = st | sp
+                continue
+            w, n, pos = p, L, L + 1
+        u2 = uniform(seed, int(rid[r]), int(pos0[r]) + pos, DRAW_CORRECT)
+        tok, dist = inverse_cdf(w, u2)
+        decisions.append(("sample", r, pos, dist))
+        n_acc[r] = n
+        for j in range(1, n + 1):
+            tokens[r, j - 1] = int(draft_tokens[r][j - 1])
+        tokens[r, n] = tok
+        status[r] = st
+
+    return {
+        "n_acc": n_acc,
+        "tokens": tokens,
+        "status": status,
+        "probe": probe,
+        "tgt_stats": tgt_stats,
+        "drf_stats": drf_stats,
+        "alpha": None,
         "decisions": decisions,
     }

@@ -247,3 +247,77 @@ def test_near_boundary_bookkeeping():
             u = rng.uniform(18, r, j, rng.DRAW_ACCEPT)
             assert np.isclose(dist, abs(u - P[j - 1][x] / Q[j - 1][x]), rtol=1e-12)
         assert dist >= 0
+
+
+def _random_batch(g, R, gmax, V, close=0.7):
+    """Reserved-slot rows: target N(0, 2^2), drafts near the targets, lengths
+    and tokens random (some outside [0, V), some with q(x) = 0)."""
+    tgt = g.normal(0, 2, (R * (gmax + 1), V))
+    drf = np.empty((R * gmax, V))
+    for r in range(R):
+        drf[r * gmax:(r + 1) * gmax] = tgt[r * (gmax + 1):r * (gmax + 1) + gmax] + g.normal(0, close, (gmax, V))
+    toks = g.integers(0, V, (R, gmax))
+    toks[g.random((R, gmax)) < 0.03] = V + 1
+    ell = g.integers(0, gmax + 1, R)
+    return tgt, drf, toks, ell
+
+
+def test_stop_at_rejection_equals_full_verification_on_usable_rows():
+    """With every row usable the outcome does not depend on the rows past the
+    first rejection, so both procedures give the same result."""
+    g = np.random.default_rng(31)
+    R, gmax, V = 60, 6, 40
+    tgt, drf, toks, ell = _random_batch(g, R, gmax, V)
+    for r in range(0, R, 7):                     # q(x) = 0 at some draft tokens
+        drf[r * gmax, min(toks[r, 0], V - 1)] = -np.inf
+    t0, d0 = np.arange(R) * (gmax + 1), np.arange(R) * gmax
+    for T in (1.0, 0.6):
+        a = Vf.verify(tgt, t0, drf, d0, toks, ell, V, T, 5)
+        b = Vf.verify_until_rejection(tgt, t0, drf, d0, toks, ell, V, T, 5)
+        assert np.array_equal(a["n_acc"], b["n_acc"])
+        assert np.array_equal(a["tokens"], b["tokens"])
+        assert np.array_equal(a["status"], b["status"])
+        assert a["decisions"] == b["decisions"]
+        for r in range(R):
+            n = b["n_acc"][r]
+            tested = min(n + 1, ell[r])          # positions whose test ran
+            assert np.array_equal(a["probe"][r, :tested], b["probe"][r, :tested])
+            assert np.array_equal(a["drf_stats"][r, :tested], b["drf_stats"][r, :tested])
+            assert np.array_equal(a["tgt_stats"][r, :tested], b["tgt_stats"][r, :tested])
+            assert np.all(b["probe"][r, tested:] == 0)
+
+
+def test_stop_at_rejection_never_reads_past_the_rejection():
+    """Rows past each request's first rejection replaced by NaN / all -inf:
+    the result is that of the clean rows; an unusable row at or before the
+    rejection (or an unusable bonus row after full acceptance) fails the
+    request, as verify() does."""
+    g = np.random.default_rng(32)
+    R, gmax, V = 40, 5, 30
+    tgt, drf, toks, ell = _random_batch(g, R, gmax, V, close=1.5)
+    t0, d0 = np.arange(R) * (gmax + 1), np.arange(R) * gmax
+    clean = Vf.verify(tgt, t0, drf, d0, toks, ell, V, 1.0, 9)
+    bad_t, bad_d = tgt.copy(), drf.copy()
+    spoiled = 0
+    for r in range(R):
+        n, L = clean["n_acc"][r], ell[r]
+        if n < L:                                # rejected at position n + 1
+            bad_t[t0[r] + n + 1:t0[r] + L + 1] = np.nan
+            bad_d[d0[r] + n + 1:d0[r] + L] = -np.inf
+            spoiled += L - n
+    assert spoiled > 20
+    lazy = Vf.verify_until_rejection(bad_t, t0, bad_d, d0, toks, ell, V, 1.0, 9)
+    for k in ("n_acc", "tokens", "status"):
+        assert np.array_equal(lazy[k], clean[k]), k
+    full = Vf.verify(bad_t, t0, bad_d, d0, toks, ell, V, 1.0, 9)
+    assert np.any(full["status"] & Vf.ST_NONFINITE)   # the full procedure reads them
+    # an unusable row at the rejected position itself, and a bad bonus row
+    r = next(r for r in range(R) if clean["n_acc"][r] < ell[r])
+    j = clean["n_acc"][r] + 1
+    t2 = tgt.copy(); t2[t0[r] + j - 1, 0] = np.nan
+    out = Vf.verify_until_rejection(t2, t0, drf, d0, toks, ell, V, 1.0, 9)
+    assert out["status"][r] == Vf.ST_NONFINITE and out["n_acc"][r] == 0 and np.all(out["tokens"][r] == -1)
+    r = next(r for r in range(R) if clean["n_acc"][r] == ell[r])
+    t3 = tgt.copy(); t3[t0[r] + ell[r]] = -np.inf
+    out = Vf.verify_until_rejection(t3, t0, drf, d0, toks, ell, V, 1.0, 9)
+    assert out["status"][r] & Vf.ST_ZERO_Z and np.all(out["tokens"][r] == -1)
