@@ -470,6 +470,30 @@ def main():
     torch.cuda.synchronize()
     ds_step_us = d0.elapsed_time(d1) / K * 1e3
 
+    # the same step reading each request's rows in rounds of positions and
+    # stopping at its first rejection (SD_VERIFY_STOP_AT_REJECTION), without
+    # and with the drafter's (m, Z)
+    def step_lazy(i, with_stats):
+        inp = sets[i % len(sets)]
+        so, vo = bufs[i % len(sets)]
+        sch = sdv.sd_schedule(inp["conf"], inp["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so,
+                              workspace=sws)
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                      sch["ell"], V, inp["temperature"], inp["seed"], workspace=ws, out=vo,
+                      drf_stats=dstats[i % len(sets)] if with_stats else None, stop_at_rejection=True)
+    lazy = {}
+    for with_stats in (False, True):
+        for i in range(len(sets)):
+            step_lazy(i, with_stats)
+        torch.cuda.synchronize()
+        same = all(torch.equal(bufs[i][1]["tokens"], ref_tokens[i]) for i in range(len(sets)))
+        d0.record()
+        for i in range(K):
+            step_lazy(i, with_stats)
+        d1.record()
+        torch.cuda.synchronize()
+        lazy[with_stats] = (d0.elapsed_time(d1) / K * 1e3, same)
+
     # schedule alone (the rest of the step is verification): its kernels are
     # shorter than the host's per-call overhead, so time a captured graph
     so = bufs[0][0]
@@ -542,6 +566,16 @@ def main():
                     "drafter (sd_verify drf_stats, as the drafting heads' q_stats give it): only "
                     "the 3072 target rows are streamed; not the headline value, which reads every "
                     "draft row too"},
+        "stop_at_rejection": {
+            "rows_per_s": round(rows / (lazy[False][0] / 1e6), 1),
+            "us_per_step": round(lazy[False][0], 1),
+            "with_drafter_stats_rows_per_s": round(rows / (lazy[True][0] / 1e6), 1),
+            "with_drafter_stats_us_per_step": round(lazy[True][0], 1),
+            "tokens_same_as_full_pass": lazy[False][1] and lazy[True][1],
+            "what": "the same step with SD_VERIFY_STOP_AT_REJECTION: each request's rows are read "
+                    "in rounds of positions (up to 2, 6, 12) and no longer once it is decided, as "
+                    "nothing after the first rejection can change the outcome; not the headline "
+                    "value, which reads every row"},
     }
     print("budget planner", file=sys.stderr, flush=True)
     result["budget_planner"] = bench_planner(sdv, torch, sets[0], bufs[0][1], bufs[0][0]["ell"])

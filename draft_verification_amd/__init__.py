@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     SD_SCHED_GLOBAL_ARGMAX,
     SD_SCHED_CAPPED_TOPK,
     SD_SCHED_THRESHOLD,
+    SD_VERIFY_STOP_AT_REJECTION,
     SD_ST_BAD_TOKEN,
     SD_ST_NONFINITE,
     SD_ST_ZERO_Z,

@@ -23,6 +23,8 @@ SD_ELAUNCH = -4
 SD_DTYPE_F32 = 0
 SD_DTYPE_BF16 = 1
 
+SD_VERIFY_STOP_AT_REJECTION = 1
+
 SD_SCHED_EARLY_STOP = 0
 SD_SCHED_GLOBAL_ARGMAX = 1
 SD_SCHED_CAPPED_TOPK = 2
@@ -77,7 +79,7 @@ def lib():
     L.sd_verify_workspace_size.argtypes = [_I, _I, _I]
     L.sd_verify.restype = _I
     L.sd_verify.argtypes = [_P, _I, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P, _P,
-                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
+                            _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P, _P]
     L.sd_markov_draft_workspace_size.restype = _SZ
     L.sd_markov_draft_workspace_size.argtypes = [_I, _I, _I, _I]
     L.sd_markov_draft.restype = _I
@@ -180,14 +182,16 @@ def sd_verify_workspace_size(R, gmax, V):
 
 def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.0, seed=0,
               pos0=None, probe=False, stats=False, alpha=False, workspace=None, out=None,
-              stream=None, prof_events=None, drf_stats=None):
+              stream=None, prof_events=None, drf_stats=None, stop_at_rejection=False):
     """Run verification.  tgt / drf: 2-D logit tensors (bf16 or fp32, ld =
     shape[1]); the rest int32 device tensors.  Returns a dict of device
     tensors: n_acc, tokens, status (and probe, row_stats, alpha if asked).
     prof_events: optional pair of raw hipEvent_t handles (ints) recorded
     around the row-statistics pass.  drf_stats: optional [R][gamma_max][2]
     fp32 (m, Z) of the draft rows (a drafting head's q_stats); the draft rows
-    are then read only where needed."""
+    are then read only where needed.  stop_at_rejection: read each request's
+    rows in rounds of positions and stop at its first rejection
+    (SD_VERIFY_STOP_AT_REJECTION; alpha must be off)."""
     R, gmax = draft_tokens.shape
     if drf_stats is not None and drf_stats.numel() != R * gmax * 2:
         raise ValueError("drf_stats must hold R * gamma_max (m, Z) pairs")
@@ -218,7 +222,7 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
         _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(ell, torch.int32, "ell"),
         _ptr(n_acc, torch.int32), _ptr(toks, torch.int32), _ptr(status, torch.int32),
         _ptr(pp, torch.float32), _ptr(rs, torch.float32), _ptr(al, torch.float32),
-        ws.data_ptr(), ws.numel(),
+        SD_VERIFY_STOP_AT_REJECTION if stop_at_rejection else 0, ws.data_ptr(), ws.numel(),
         *(prof_events if prof_events else (None, None)))
     _check("sd_verify", code)
     return dict(n_acc=n_acc, tokens=toks, status=status, probe=pp, row_stats=rs, alpha=al)

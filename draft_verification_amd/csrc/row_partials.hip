@@ -10,7 +10,9 @@
 // then sum 2^(x*c - fp32(max*c)) in registers, and each wave leaves one
 // partial (max, sum).  No LDS, no barrier.  Workgroups of rows outside the
 // scheduled batch exit at once.  When the drafter hands over its rows'
-// statistics the pass covers the target rows alone.
+// statistics the pass covers the target rows alone; when verification stops
+// at each request's first rejection it runs once per round of positions,
+// the later rounds over the list of requests still undecided.
 #include "sdv_host.h"
 #include "verify_common.h"
 
@@ -21,17 +23,14 @@ using sdv::kNegInf;
 using sdv::kRowThreads;
 using sdv::kRowWaves;
 
+// One chunk of one row: the partials of its four waves.
 template <bool BF16>
-__global__ __launch_bounds__(kRowThreads) void k_row_partials(sdv::RowPassArgs a) {
+__device__ __forceinline__ void row_chunk(const sdv::RowPassArgs& a, int r, int slot, int ch) {
   using VT = sdv::Vec<BF16>;
   constexpr int kVec = kChunk / VT::kElems / kRowThreads;
-  const int item = blockIdx.x;
-  const int ch = item % a.n_ch;
-  const int rl = item / a.n_ch;
-  const int slot = rl % a.slots, r = rl / a.slots;
-  const int rs = r * (2 * a.gmax + 1) + slot;  // row of the partials' layout
   const int L = sdv::clampi(a.ell[r], 0, a.gmax);
   if (!sdv::slot_in_batch(slot, a.gmax, L)) return;
+  const int rs = r * (2 * a.gmax + 1) + slot;  // row of the partials' layout
   const char* row = slot <= a.gmax
                         ? a.tgt + ((int64_t)a.tgt_row0[r] + slot) * a.ld_bytes
                         : a.drf + ((int64_t)a.drf_row0[r] + (slot - a.gmax - 1)) * a.ld_bytes;
@@ -72,13 +71,42 @@ __global__ __launch_bounds__(kRowThreads) void k_row_partials(sdv::RowPassArgs a
     a.partial[((size_t)rs * a.n_ch + ch) * kRowWaves + (threadIdx.x >> 6)] = make_float2(wm, ws);
 }
 
+// Item -> (request index, slot, chunk) in the pass's ranges.
+__device__ __forceinline__ void item_slot(const sdv::RowPassArgs& a, int item, int* ri, int* slot, int* ch) {
+  *ch = item % a.n_ch;
+  const int rl = item / a.n_ch;
+  const int sl = rl % a.slots, nt = a.t_hi - a.t_lo;
+  *ri = rl / a.slots;
+  *slot = sl < nt ? a.t_lo + sl : a.gmax + a.d_lo + (sl - nt);
+}
+
+template <bool BF16, bool LIST>
+__global__ __launch_bounds__(kRowThreads) void k_row_partials(sdv::RowPassArgs a) {
+  if (a.clear && blockIdx.x == 0 && threadIdx.x == 0) *a.clear = 0;
+  int ri, slot, ch;
+  if constexpr (!LIST) {
+    item_slot(a, blockIdx.x, &ri, &slot, &ch);
+    row_chunk<BF16>(a, ri, slot, ch);
+  } else {  // the listed requests' items, strided over the grid
+    const int n_items = *a.count * a.slots * a.n_ch;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      item_slot(a, item, &ri, &slot, &ch);
+      row_chunk<BF16>(a, a.list[ri], slot, ch);
+    }
+  }
+}
+
 }  // namespace
 
 namespace sdv {
 
-hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned items, hipStream_t stream) {
-  if (bf16) return launch(k_row_partials<true>, dim3(items), dim3(kRowThreads), 0, stream, a);
-  return launch(k_row_partials<false>, dim3(items), dim3(kRowThreads), 0, stream, a);
+hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned grid, hipStream_t stream) {
+  if (a.list) {
+    if (bf16) return launch(k_row_partials<true, true>, dim3(grid), dim3(kRowThreads), 0, stream, a);
+    return launch(k_row_partials<false, true>, dim3(grid), dim3(kRowThreads), 0, stream, a);
+  }
+  if (bf16) return launch(k_row_partials<true, false>, dim3(grid), dim3(kRowThreads), 0, stream, a);
+  return launch(k_row_partials<false, false>, dim3(grid), dim3(kRowThreads), 0, stream, a);
 }
 
 }  // namespace sdv

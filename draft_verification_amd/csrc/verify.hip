@@ -24,11 +24,19 @@
 //                   u * sum(w) with a workgroup prefix sum, and one wave scans
 //                   that block.  A bonus draw locates its chunk from the first
 //                   pass's partials and rescans only that chunk.
+//
+// Verification that stops at each request's first rejection runs the
+// bandwidth pass and the deciding half of k_finish in rounds of positions
+// (up to 2, 6, 14, ...): a round decides the requests that rejected, failed
+// or reached their bonus row and lists the others for the next round; then
+// one k_finish launch makes every recorded draw at once.
 //   k_alpha_sums,   only when the acceptance rates are asked for: sums of
 //   k_alpha_total   min(p, q) per (request, position, chunk), then per row -
 //                   the probability that the position is accepted, which is
 //                   1 - TV(p, q), the confidence label of the DSpark summary
 //                   ("2.1")
+#include <algorithm>
+
 #include "sdv_host.h"
 #include "verify_common.h"
 
@@ -47,9 +55,20 @@ constexpr int kStagedParts = 4096;                  // partials of one request s
 constexpr int kLdsBlocks = 2048;                    // residual block sums kept in LDS (V <= 2M)
 constexpr int kAlphaThreads = 256;
 constexpr int kNone = 0x7FFFFFFF;
+constexpr int kMaxRounds = 8;          // position rounds 2, 6, 14, ..., 510 > SD_MAX_GAMMA + 1
+constexpr unsigned kListGrid = 4096;   // workgroups of a listed round's bandwidth pass
 static_assert(kChunkBlocks == kFinWaves, "a bonus chunk is rescanned one block per wave");
 static_assert(sdv::kMaxChunks <= kFinThreads, "chunk locate assumes one chunk per thread");
 static_assert(SD_MAX_GAMMA < kFinThreads, "one accept test per thread");
+
+// The correction draw a request was decided on.
+struct DrawRec {
+  int kind;              // 0: nothing to draw (the request failed), 1: residual, 2: target row
+  int n;                 // drafts accepted
+  int st;                // status bits so far
+  int pos;               // position of the drawn token
+  float mct, izt, mcd, izd;  // the rows' references and fp32(1 / Z) (draft row: kind 1)
+};
 
 struct VerifyArgs {
   const char* tgt;
@@ -71,6 +90,17 @@ struct VerifyArgs {
   double* row_z;          // [R][S] sum 2^(x*c - ref)
   double* bsum;           // [R][n_blk] residual mass per 1024-element block
   double* asum;           // [R][gmax][n_ch][kRowWaves] chunk sums of min(p, q)
+  // Rounds (verification that stops at each request's first rejection): the
+  // rows read so far are the target slots < cover and the draft positions
+  // <= cover; `list`/`count` name the requests of this round (null: all),
+  // and an undecided request is appended to next_list/next_count.
+  const int32_t* list;
+  const int32_t* count;
+  int32_t* next_list;
+  int32_t* next_count;
+  int cover;              // gmax + 1 covers every row
+  int stop_at_rejection;  // rows past the first rejection are not needed
+  DrawRec* recs;          // [R] decided draws, when the draws run in a kernel of their own
   int64_t ld_bytes;
   uint64_t seed;
   float c;                // log2(e) / T
@@ -169,30 +199,35 @@ __device__ __forceinline__ double block_incl_scan(double v, int lane, int wave, 
 }
 
 // ---------------------------------------------------------------------------
+// Request r, up to its correction draw: the rows' (m, Z), the accept tests
+// and the decision.  Returns true with the draw to make in *rec; false when
+// the request failed (its outputs written) or is not decided yet (listed for
+// the next round).
 template <bool BF16>
-__global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
+__device__ __forceinline__ bool finish_decide(const VerifyArgs& a, int r, DrawRec* rec) {
   using VT = sdv::Vec<BF16>;
-  constexpr int VL = kBlk / VT::kElems / 64;  // vectors per lane per row of a block
-  constexpr int kBlkVec = kBlk / VT::kElems;
   __shared__ float sRef[kMaxSlots];
   __shared__ double sZ[kMaxSlots];
   __shared__ float2 sPart[kStagedParts];
-  __shared__ double s_incl[kFinThreads];
-  __shared__ double s_bs[kLdsBlocks];
-  __shared__ double s_w[kFinWaves];
-  __shared__ int s_st, s_jstar, s_zero_q_upto, s_owner, s_blk, s_tok, s_last;
-  __shared__ double s_rem;
+  __shared__ int s_rst[kMaxSlots];  // status bits of each unusable row
+  __shared__ int s_st, s_jb, s_jstar, s_zero_q_upto;
 
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int gmax = a.gmax, S = 2 * gmax + 1, V = a.V;
   const int L = sdv::clampi(a.ell[r], 0, gmax);
   const int nparts = a.n_ch * kRowWaves;
   const float c = a.c;
+  // rows read so far: target slots 0..nT-1, draft positions 1..Lt (the
+  // positions tested in this round)
+  const int Lt = min(L, a.cover);
+  const int nT = min(L, a.cover - 1) + 1;
+  const bool lazy = a.stop_at_rejection != 0;
+  for (int i = tid; i < kMaxSlots; i += kFinThreads) s_rst[i] = 0;
   if (tid == 0) {
     s_st = 0;
-    s_jstar = L + 1;
+    s_jb = kNone;
+    s_jstar = Lt + 1;
     s_zero_q_upto = kNone;
-    s_owner = kNone;
   }
 
   // The accept tests' operands (thread j-1 tests position j: the drafted
@@ -203,7 +238,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   int xj = -1;
   float ltj = 0.0f, ldj = 0.0f;
   float2 mzj = make_float2(0.0f, 0.0f);
-  if (jt <= L) {
+  if (jt <= Lt) {
     xj = drafts[jt - 1];
     if (a.drf_stats) mzj = a.drf_stats[(size_t)r * gmax + (jt - 1)];
     if (xj >= 0 && xj < V) {
@@ -212,25 +247,38 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
     }
   }
 
-  // Stage the partials of the batch rows (target slots 0..L, then draft slots
-  // gmax+1..gmax+L unless their statistics were supplied, i.e. local row b)
-  // in LDS when they fit: one load each.
-  const int nrows = a.drf_stats ? L + 1 : 2 * L + 1;
+  // Stage the partials of the rows read (target slots 0..nT-1, then draft
+  // slots gmax+1..gmax+Lt unless their statistics were supplied, i.e. local
+  // row b) in LDS when they fit: one load each.
+  const int nrows = a.drf_stats ? nT : nT + Lt;
   const bool staged = (long long)nrows * nparts <= kStagedParts;
   const float2* base = a.partial + (size_t)r * S * nparts;
   if (staged) {
     for (int i = tid; i < nrows * nparts; i += kFinThreads) {
       const int b = i / nparts, q = i % nparts;
-      const int slot = b <= L ? b : gmax + (b - L);
+      const int slot = b < nT ? b : gmax + 1 + (b - nT);
       sPart[i] = base[(size_t)slot * nparts + q];
     }
   }
   __syncthreads();
 
+  // An unusable row fails the request: any row of the batch, or, when rows
+  // past the first rejection are not needed, a row at or before it (the
+  // first position whose target or draft row is unusable, s_jb, is kept;
+  // target slot s serves position s + 1, the bonus row position L + 1).
+  auto unusable = [&](int slot, int st) {
+    if (!lazy) {
+      atomicOr(&s_st, st);
+    } else {
+      s_rst[slot] = st;
+      atomicMin(&s_jb, slot <= gmax ? slot + 1 : slot - gmax);
+    }
+  };
+
   // (m, Z) per row: groups of 16 lanes, one row per group at a time
   const int grp = tid >> 4, gl = tid & 15;
   for (int b = grp; b < nrows; b += kFinThreads / 16) {
-    const int slot = b <= L ? b : gmax + (b - L);
+    const int slot = b < nT ? b : gmax + 1 + (b - nT);
     const float2* pp = staged ? sPart + b * nparts : base + (size_t)slot * nparts;
     float M = kNegInf;
     for (int q = gl; q < nparts; q += 16) M = fmaxf(M, pp[q].x);
@@ -250,17 +298,17 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
       a.row_ref[(size_t)r * S + slot] = ref;
       a.row_z[(size_t)r * S + slot] = Z;
       const int st = row_status(M, Z);
-      if (st) atomicOr(&s_st, st);
+      if (st) unusable(slot, st);
       if (a.row_stats)
         ((float2*)a.row_stats)[(size_t)r * S + slot] = sdv::stats_report(M, ref, Z, a.inv_t);
     }
   }
-  if (a.drf_stats && jt <= L) {  // the drafter's statistics of draft row jt
+  if (a.drf_stats && jt <= Lt) {  // the drafter's statistics of draft row jt
     const int slot = gmax + jt;
     float ref;
     double Z;
     const int st = sdv::stats_read(mzj, &ref, &Z);
-    if (st) atomicOr(&s_st, st);
+    if (st) unusable(slot, st);
     sRef[slot] = ref;
     sZ[slot] = Z;
     a.row_ref[(size_t)r * S + slot] = ref;
@@ -270,18 +318,23 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   __syncthreads();
 
   int32_t* out_tok = a.out_tokens + (size_t)r * (gmax + 1);
-  if (s_st) {  // a needed row is unusable: the request fails
+  auto fail = [&](int st) {  // the request fails: no token
     for (int t = tid; t <= gmax; t += kFinThreads) out_tok[t] = -1;
     if (tid == 0) {
       a.n_accepted[r] = 0;
-      a.status[r] = s_st;
+      a.status[r] = st;
     }
-    return;
+  };
+  if (s_st) {  // a needed row is unusable
+    fail(s_st);
+    return false;
   }
+  const int jb = s_jb;  // kNone unless rows past the first rejection are not needed
 
-  // every accept test at once; the chain stops at the first rejection
+  // every accept test at once (before the first unusable row); the chain
+  // stops at the first rejection
   const int64_t pbase = a.pos0 ? a.pos0[r] : 0;
-  if (jt <= L) {
+  if (jt <= Lt && jt < jb) {
     const int j = jt, x = xj;
     bool reject;
     if (x < 0 || x >= V) {
@@ -307,7 +360,15 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   __syncthreads();
 
   const int jstar = s_jstar;
-  const bool rejected = jstar <= L;
+  const bool rejected = jstar <= Lt;
+  if (jb != kNone && !rejected) {  // an unusable row before any rejection
+    fail(s_rst[jb - 1] | (jb <= gmax ? s_rst[gmax + jb] : 0));
+    return false;
+  }
+  if (!rejected && L >= a.cover) {  // all accepted so far; the rest is not read yet
+    if (tid == 0) a.next_list[atomicAdd(a.next_count, 1)] = r;
+    return false;
+  }
   const int n = rejected ? jstar - 1 : L;
   for (int t = tid; t <= gmax; t += kFinThreads) out_tok[t] = (t < n) ? drafts[t] : -1;
   int st = 0;
@@ -317,19 +378,53 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
     if (x < 0 || x >= V) st |= SD_ST_BAD_TOKEN;
   }
 
-  // The correction draw.
   const int pos = rejected ? jstar : L + 1;
+  rec->kind = rejected ? 1 : 2;
+  rec->n = n;
+  rec->st = st;
+  rec->pos = pos;
+  rec->mct = sRef[pos - 1];
+  rec->izt = (float)(1.0 / sZ[pos - 1]);
+  rec->mcd = rejected ? sRef[gmax + jstar] : 0.0f;
+  rec->izd = rejected ? (float)(1.0 / sZ[gmax + jstar]) : 1.0f;
+  return true;
+}
+
+// The correction draw of request r (every thread of the workgroup): the
+// residual max(0, p - q) of the rejected position or the target row after
+// the last draft, by inverse CDF; writes the token, n_accepted and status.
+template <bool BF16>
+__device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec rec) {
+  using VT = sdv::Vec<BF16>;
+  constexpr int VL = kBlk / VT::kElems / 64;  // vectors per lane per row of a block
+  constexpr int kBlkVec = kBlk / VT::kElems;
+  __shared__ double s_incl[kFinThreads];
+  __shared__ double s_bs[kLdsBlocks];
+  __shared__ double s_w[kFinWaves];
+  __shared__ int s_owner, s_blk, s_tok, s_last;
+  __shared__ double s_rem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gmax = a.gmax, S = 2 * gmax + 1, V = a.V;
+  const int nparts = a.n_ch * kRowWaves;
+  const float c = a.c;
+  const int64_t pbase = a.pos0 ? a.pos0[r] : 0;
+  int32_t* out_tok = a.out_tokens + (size_t)r * (gmax + 1);
+  const int n = rec.n, pos = rec.pos;
+  int st = rec.st;
+  if (tid == 0) s_owner = kNone;  // read after the first prefix sum's barriers
+
   const double u = sdv::uniform24(a.seed, (uint64_t)r, (uint64_t)(pbase + pos), 2);
   const int tslot = pos - 1;
   const char* trow = a.tgt + ((int64_t)a.tgt_row0[r] + (pos - 1)) * a.ld_bytes;
-  const char* drow = rejected ? a.drf + ((int64_t)a.drf_row0[r] + (jstar - 1)) * a.ld_bytes : trow;
+  const char* drow = rec.kind == 1 ? a.drf + ((int64_t)a.drf_row0[r] + (pos - 1)) * a.ld_bytes : trow;
   DrawParams dp;
-  dp.kind = rejected ? 1 : 2;
+  dp.kind = rec.kind;
   dp.c = c;
-  dp.mct = sRef[tslot];
-  dp.izt = (float)(1.0 / sZ[tslot]);
-  dp.mcd = rejected ? sRef[gmax + jstar] : 0.0f;
-  dp.izd = rejected ? (float)(1.0 / sZ[gmax + jstar]) : 1.0f;
+  dp.mct = rec.mct;
+  dp.izt = rec.izt;
+  dp.mcd = rec.mcd;
+  dp.izd = rec.izd;
   const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
   const int nvec = V / VT::kElems;
   const uint4* tp = (const uint4*)trow;
@@ -526,6 +621,35 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   }
 }
 
+// The finishing kernel, one workgroup per request: decide and draw at once
+// (every row read in one pass), or in rounds: decide only (the draws
+// recorded), then every recorded draw at once.
+enum { kFused = 0, kDecide = 1, kDraw = 2 };
+
+template <bool BF16, int PHASE>
+__global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
+  DrawRec rec;
+  int r;
+  if constexpr (PHASE == kDraw) {
+    r = (int)blockIdx.x;
+    rec = a.recs[r];
+    if (rec.kind == 0) return;  // failed: outputs already written
+  } else {
+    if (a.list && (int)blockIdx.x >= *a.count) return;
+    r = a.list ? a.list[blockIdx.x] : (int)blockIdx.x;
+    const bool draw = finish_decide<BF16>(a, r, &rec);
+    if constexpr (PHASE == kDecide) {
+      if (threadIdx.x == 0) {
+        if (!draw) rec.kind = 0;  // failed, or decided in a later round
+        a.recs[r] = rec;
+      }
+      return;
+    }
+    if (!draw) return;
+  }
+  finish_draw<BF16>(a, r, rec);
+}
+
 // ---------------------------------------------------------------------------
 // Acceptance rate of position j: sum over the vocabulary of min(p_j, q_j).
 template <bool BF16>
@@ -604,12 +728,19 @@ size_t verify_ws_bytes(int R, int gmax, int V) {
   return partial_bytes(R, gmax, V) + sdv_align256((size_t)R * S * sizeof(float)) +
          sdv_align256((size_t)R * S * sizeof(double)) +
          sdv_align256((size_t)R * n_blk * sizeof(double)) +
-         sdv_align256((size_t)R * gmax * n_ch * kRowWaves * sizeof(double));
+         sdv_align256((size_t)R * gmax * n_ch * kRowWaves * sizeof(double)) +
+         sdv_align256((size_t)kMaxRounds * (R + 1) * sizeof(int32_t)) +
+         sdv_align256((size_t)R * sizeof(DrawRec));
 }
 
-template <bool BF16>
+// Rounds of positions when verification stops at the first rejection: the
+// rows of positions up to 2, 6, 14, ... are read in turn, each round only
+// for the requests that accepted every position so far.
+int next_cover(int cover) { return 2 * cover + 2; }
+
+template <bool BF16, int PHASE>
 int launch_finish(hipStream_t stream, int R, const VerifyArgs& a) {
-  SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16>, dim3(R), dim3(kFinThreads), 0, stream, a));
+  SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16, PHASE>, dim3(R), dim3(kFinThreads), 0, stream, a));
   if (a.accept_prob && a.gmax > 0) {
     SDV_TRY_LAUNCH(sdv::launch(k_alpha_sums<BF16>, dim3((unsigned)((long long)R * a.gmax * a.n_ch)),
                                dim3(sdv::kRowThreads), 0, stream, a));
@@ -632,13 +763,16 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
                          const int32_t* drf_row0, const float* drf_stats, const int32_t* draft_tokens,
                          const int32_t* ell, int32_t* n_accepted, int32_t* out_tokens,
                          int32_t* status, float* probe_probs, float* row_stats,
-                         float* accept_prob, void* workspace, size_t workspace_bytes,
+                         float* accept_prob, int options, void* workspace, size_t workspace_bytes,
                          hipEvent_t prof_start, hipEvent_t prof_stop) {
   if (R < 0 || gamma_max < 0 || V < 8 || (V % 8) != 0 || ld < V || (ld % 8) != 0) return SD_EINVAL;
   if (gamma_max > SD_MAX_GAMMA || V > SD_MAX_VOCAB) return SD_EUNSUPPORTED;
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_EINVAL;
   if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf())) return SD_EINVAL;
   if ((prof_start == nullptr) != (prof_stop == nullptr)) return SD_EINVAL;
+  if ((options & ~SD_VERIFY_STOP_AT_REJECTION) != 0) return SD_EINVAL;
+  const bool lazy = (options & SD_VERIFY_STOP_AT_REJECTION) != 0;
+  if (lazy && accept_prob) return SD_EINVAL;  // acceptance rates need every row
   if (R == 0) return SD_OK;
   if (!tgt_logits || !tgt_row0 || !drf_row0 || !ell || !n_accepted || !out_tokens || !status)
     return SD_EINVAL;
@@ -649,8 +783,7 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
     return SD_EINVAL;
   if ((((uintptr_t)drf_stats) & 7) != 0 || (((uintptr_t)row_stats) & 7) != 0) return SD_EINVAL;
   const int n_ch = (V + kChunk - 1) / kChunk;
-  const int slots = drf_stats ? gamma_max + 1 : 2 * gamma_max + 1;  // rows the bandwidth pass reads
-  const long long items = (long long)R * slots * n_ch;
+  const long long items = (long long)R * (2 * gamma_max + 1) * n_ch;  // the largest pass
   if (items > 0xFFFFFFFFLL / sdv::kRowThreads) return SD_EUNSUPPORTED;  // work-items of one launch
   const int64_t ld_bytes = (int64_t)ld * (dtype == SD_DTYPE_BF16 ? 2 : 4);
   const float c = sdv::kLog2e / temperature;
@@ -674,7 +807,18 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   ra.gmax = gamma_max;
   ra.V = V;
   ra.n_ch = n_ch;
-  ra.slots = slots;
+  ra.list = nullptr;
+  ra.count = nullptr;
+  ra.clear = nullptr;
+  // target slots [t_lo, t_hi) and draft positions [d_lo, d_hi] of one pass
+  auto set_range = [&](int t_lo, int t_hi, int d_lo, int d_hi) {
+    if (drf_stats) d_hi = d_lo - 1;  // the drafter's statistics replace the draft rows
+    ra.t_lo = t_lo;
+    ra.t_hi = t_hi;
+    ra.d_lo = d_lo;
+    ra.d_hi = d_hi;
+    ra.slots = (t_hi - t_lo) + (d_hi >= d_lo ? d_hi - d_lo + 1 : 0);
+  };
 
   VerifyArgs a;
   a.tgt = (const char*)tgt_logits;
@@ -699,6 +843,17 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   a.bsum = (double*)p;
   p += sdv_align256((size_t)R * n_blk * sizeof(double));
   a.asum = (double*)p;
+  p += sdv_align256((size_t)R * gamma_max * n_ch * kRowWaves * sizeof(double));
+  int32_t* lists = (int32_t*)p;                          // [kMaxRounds][R]
+  int32_t* counts = lists + (size_t)kMaxRounds * R;      // [kMaxRounds]
+  p += sdv_align256((size_t)kMaxRounds * (R + 1) * sizeof(int32_t));
+  a.recs = (DrawRec*)p;                                  // [R]
+  a.list = nullptr;
+  a.count = nullptr;
+  a.next_list = nullptr;
+  a.next_count = nullptr;
+  a.cover = gamma_max + 1;
+  a.stop_at_rejection = lazy ? 1 : 0;
   a.ld_bytes = ld_bytes;
   a.seed = seed;
   a.c = c;
@@ -709,8 +864,42 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   a.n_blk = n_blk;
 
   const bool bf16 = dtype == SD_DTYPE_BF16;
-  if (prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
-  SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, (unsigned)items, stream));
-  if (prof_stop) SDV_TRY_LAUNCH(hipEventRecord(prof_stop, stream));
-  return bf16 ? launch_finish<true>(stream, R, a) : launch_finish<false>(stream, R, a);
+  if (!lazy) {  // every row of the batch in one pass
+    set_range(0, gamma_max + 1, 1, gamma_max);
+    if (prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
+    SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, (unsigned)((long long)R * ra.slots * n_ch), stream));
+    if (prof_stop) SDV_TRY_LAUNCH(hipEventRecord(prof_stop, stream));
+    return bf16 ? launch_finish<true, kFused>(stream, R, a) : launch_finish<false, kFused>(stream, R, a);
+  }
+  // Rounds of positions: round k reads target slots [prev, cover) and draft
+  // positions (prev, cover] of the requests still undecided (every request
+  // in round 0), then decides those that rejected, failed, or reached their
+  // bonus row, and lists the others for round k + 1.  The draws of all
+  // requests then run at once.
+  int prev = 0;
+  for (int k = 0; prev < gamma_max + 1; ++k) {
+    const int cover = std::min(next_cover(prev), gamma_max + 1);
+    const bool last = cover == gamma_max + 1;
+    set_range(prev, cover, prev + 1, std::min(cover, gamma_max));
+    ra.list = k ? lists + (size_t)k * R : nullptr;
+    ra.count = k ? counts + k : nullptr;
+    ra.clear = last ? nullptr : counts + k + 1;
+    const long long n_items = (long long)R * ra.slots * n_ch;
+    const unsigned grid = k ? (unsigned)std::min<long long>(n_items, kListGrid) : (unsigned)n_items;
+    if (k == 0 && prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
+    if (grid > 0) SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, grid, stream));
+    if (k == 0 && prof_stop) SDV_TRY_LAUNCH(hipEventRecord(prof_stop, stream));
+    a.cover = cover;
+    a.list = ra.list;
+    a.count = ra.count;
+    a.next_list = last ? nullptr : lists + (size_t)(k + 1) * R;
+    a.next_count = last ? nullptr : counts + k + 1;
+    const int rc =
+        bf16 ? launch_finish<true, kDecide>(stream, R, a) : launch_finish<false, kDecide>(stream, R, a);
+    if (rc != SD_OK) return rc;
+    prev = cover;
+  }
+  a.list = nullptr;
+  a.count = nullptr;
+  return bf16 ? launch_finish<true, kDraw>(stream, R, a) : launch_finish<false, kDraw>(stream, R, a);
 }

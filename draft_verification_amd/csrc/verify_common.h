@@ -51,7 +51,11 @@ SDV_DEV bool slot_in_batch(int slot, int gmax, int L) {
   return slot <= gmax ? slot <= L : slot - gmax <= L;
 }
 
-// Arguments of the bandwidth pass.
+// Arguments of the bandwidth pass.  One pass covers, of every listed request,
+// the target slots [t_lo, t_hi) and the draft positions [d_lo, d_hi] (draft
+// position j is slot gmax + j of the partials' layout), within the scheduled
+// batch: all of them in one pass, or a range of positions per round when
+// verification stops at each request's first rejection.
 struct RowPassArgs {
   const char* tgt;
   const int32_t* tgt_row0;
@@ -64,12 +68,17 @@ struct RowPassArgs {
   int gmax;
   int V;
   int n_ch;
-  int slots;        // leading slots of each request the pass covers: 2*gmax+1,
-                    // or gmax+1 (target rows only) when the drafter's
-                    // statistics replace the draft rows
+  int t_lo, t_hi;   // target slots [t_lo, t_hi)
+  int d_lo, d_hi;   // draft positions [d_lo, d_hi]; none when d_lo > d_hi (the
+                    // drafter's statistics replace the draft rows)
+  int slots;        // (t_hi - t_lo) + number of draft positions
+  const int32_t* list;   // the requests of this pass (null: every request) ...
+  const int32_t* count;  // ... and their number
+  int32_t* clear;        // counter the next round appends to, zeroed here (or null)
 };
 
-// Launch the bandwidth pass over items = R * slots * n_ch workgroups.
-hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned items, hipStream_t stream);
+// Launch the bandwidth pass: one workgroup per (request, slot, chunk) item
+// without a list, else `grid` workgroups striding over the listed items.
+hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned grid, hipStream_t stream);
 
 }  // namespace sdv

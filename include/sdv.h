@@ -69,6 +69,9 @@ extern "C" {
 #define SD_DTYPE_F32   0
 #define SD_DTYPE_BF16  1
 
+/* sd_verify options */
+#define SD_VERIFY_STOP_AT_REJECTION 1
+
 /* scheduler modes [DS 2.2, challenge 2] */
 #define SD_SCHED_EARLY_STOP     0
 #define SD_SCHED_GLOBAL_ARGMAX  1
@@ -200,14 +203,27 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *               trained on [DS 2.1]; 0 past ell and for a failed request.
  *               Costs a second read of every verified row pair (not done
  *               when NULL).
+ * options     0 or SD_VERIFY_STOP_AT_REJECTION.  Everything after the first
+ *             rejection is discarded [SD 1.1], so the rows past it cannot
+ *             change the outcome; with this option each request's rows are
+ *             read in rounds of positions (up to 2, 6, 14, ...) and a request
+ *             stops being read once it is decided.  On usable rows the
+ *             result is the same; a row past the first rejection is never
+ *             read, so it fails nothing (a position fails the request only
+ *             when its own target or draft row is unusable, the bonus row
+ *             only after full acceptance); row_stats and probe_probs are
+ *             written for the rows and positions examined only; accept_prob
+ *             must be NULL.
  * prof_start, prof_stop  optional HIP events (both or neither): recorded on
  *             `stream` right before and after the row-statistics pass (the
- *             bandwidth-bound kernel that streams every row once), so a caller
- *             can time that pass alone.
+ *             bandwidth-bound kernel that streams every row once; its first
+ *             round under SD_VERIFY_STOP_AT_REJECTION), so a caller can time
+ *             that pass alone.
  * Degenerate data (mirrors the CPU reference): a token outside [0, V) at a
  * tested position sets BAD_TOKEN and counts as a rejection; a needed row with
  * NaN / +inf (NONFINITE) or all -inf (ZERO_Z) fails the request: n_accepted 0
- * and every output token -1; an empty residual sets ZERO_RESIDUAL and the
+ * and every output token -1 (every batch row is needed, or under
+ * SD_VERIFY_STOP_AT_REJECTION the rows up to the first rejection); an empty residual sets ZERO_RESIDUAL and the
  * token is drawn from p_j*; q(x) = 0 sets ZERO_Q (accepted iff p(x) > 0).
  */
 size_t sd_verify_workspace_size(int R, int gamma_max, int V);
@@ -217,7 +233,7 @@ int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype
               const void* drf_logits, const int32_t* drf_row0, const float* drf_stats,
               const int32_t* draft_tokens, const int32_t* ell,
               int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
-              float* probe_probs, float* row_stats, float* accept_prob,
+              float* probe_probs, float* row_stats, float* accept_prob, int options,
               void* workspace, size_t workspace_bytes,
               hipEvent_t prof_start, hipEvent_t prof_stop);
 

@@ -26,10 +26,11 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-def oracle_verify_subset(inp, reqs, ell):
+def oracle_verify_subset(inp, reqs, ell, stop_at_rejection=False):
     """Oracle verification of requests `reqs` of a reserved-slot-layout input,
     keeping their true request indices for the uniforms.  Only the rows of
-    those requests are copied to the host."""
+    those requests are copied to the host.  stop_at_rejection: the oracle
+    that reads positions in order and stops at the first rejection."""
     V = inp["V"]
     t0 = to_np(inp["tgt_row0"]).astype(np.int64)
     d0 = to_np(inp["drf_row0"]).astype(np.int64)
@@ -52,8 +53,9 @@ def oracle_verify_subset(inp, reqs, ell):
     tgt = gather(inp["tgt"], tgt_rows)
     drf = gather(inp["drf"], drf_rows)
     pos0 = None if inp.get("pos0") is None else to_np(inp["pos0"])[list(reqs)]
-    return OV.verify(tgt, np.array(tr0), drf, np.array(dr0), toks[list(reqs)], ell[list(reqs)],
-                     V, inp["temperature"], inp["seed"], pos0, req_ids=list(reqs))
+    fn = OV.verify_until_rejection if stop_at_rejection else OV.verify
+    return fn(tgt, np.array(tr0), drf, np.array(dr0), toks[list(reqs)], ell[list(reqs)],
+              V, inp["temperature"], inp["seed"], pos0, req_ids=list(reqs))
 
 
 def compare_verify(gpu, ora, reqs):
@@ -116,6 +118,27 @@ def cdf_shift(L_gpu, L_ora, V, T):
     if mm is None or mm[0] >= 0.5:
         return np.inf
     return 2.0 * mm[0] / (1.0 - mm[0])
+
+
+def check_examined_stats(gpu, ora, reqs, ell, gmax):
+    """As check_stats for verification that stops at the first rejection:
+    the rows and positions the oracle examined (up to each request's decided
+    position), which the GPU has read too."""
+    rs = to_np(gpu["row_stats"])
+    pr = to_np(gpu["probe"])
+    for i, r in enumerate(reqs):
+        if ora["status"][i] & (OV.ST_NONFINITE | OV.ST_ZERO_Z):
+            continue
+        L, n = int(ell[r]), int(ora["n_acc"][i])
+        tmax = n if n < L else L             # target slots read: 0..tmax
+        dmax = n + 1 if n < L else L         # draft positions read: 1..dmax
+        assert_rel(rs[r, :tmax + 1, 0], ora["tgt_stats"][i, :tmax + 1, 0], what=f"r{r} target m", atol=REL)
+        assert_rel(rs[r, :tmax + 1, 1], ora["tgt_stats"][i, :tmax + 1, 1], what=f"r{r} target Z")
+        assert_rel(rs[r, gmax + 1:gmax + 1 + dmax, 0], ora["drf_stats"][i, :dmax, 0], what=f"r{r} draft m",
+                   atol=REL)
+        assert_rel(rs[r, gmax + 1:gmax + 1 + dmax, 1], ora["drf_stats"][i, :dmax, 1], what=f"r{r} draft Z")
+        ok = ora["probe"][i, :dmax, 1] > 0
+        assert_rel(pr[r, :dmax][ok], ora["probe"][i, :dmax][ok], what=f"r{r} probe p,q")
 
 
 def check_drafted_row_stats(mz_gpu, L_gpu, L_ora, V, T, what=""):

@@ -65,13 +65,14 @@ def test_schedule_host_validation():
     assert _sched(4, 4, 0, 20, ws=64) == _lib.SD_ERANGE          # workspace < 16 keys
 
 
-def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=(), dstats=None, rstats=None):
+def _ver(R=2, g=2, V=64, ld=64, dt=1, T=1.0, ws=1 << 20, ws_ptr=256, nulls=(), dstats=None, rstats=None,
+         alpha=None, options=0):
     L = sdv.lib()
     P = lambda name: None if name in nulls else ctypes.c_void_p(256)
     opt = lambda a: None if a is None else ctypes.c_void_p(a)
     return L.sd_verify(None, R, g, V, ld, dt, T, 1, None, P("tgt"), P("t0"), P("drf"), P("d0"),
                        opt(dstats), P("toks"), P("ell"), P("nacc"), P("out"), P("st"), None,
-                       opt(rstats), None, ctypes.c_void_p(ws_ptr), ws, None, None)
+                       opt(rstats), opt(alpha), options, ctypes.c_void_p(ws_ptr), ws, None, None)
 
 
 def test_verify_host_validation():
@@ -87,6 +88,8 @@ def test_verify_host_validation():
     assert _ver(nulls=("tgt",)) == _lib.SD_EINVAL
     assert _ver(nulls=("ell",)) == _lib.SD_EINVAL
     assert _ver(R=0) == _lib.SD_OK                                  # nothing to do
+    assert _ver(options=2) == _lib.SD_EINVAL                        # unknown option
+    assert _ver(options=sdv.SD_VERIFY_STOP_AT_REJECTION, alpha=256) == _lib.SD_EINVAL  # alpha needs every row
     assert _ver(dstats=260) == _lib.SD_EINVAL                       # (m, Z) pairs need 8 bytes
     assert _ver(rstats=260) == _lib.SD_EINVAL
     # 1024 requests x 511 rows x 64 chunks: more work-items than one launch holds

@@ -15,7 +15,8 @@ import torch
 import draft_verification_amd as sdv
 from oracle import schedule as OS
 from workloads import verify_config, verify_inputs
-from tests.parity_util import (oracle_verify_subset, compare_verify, check_stats, to_np)
+from tests.parity_util import (oracle_verify_subset, compare_verify, check_stats, check_examined_stats,
+                               to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -271,3 +272,111 @@ def test_verify_headline_with_draft_statistics_sampled():
     full, _ = _full_check(inp, ell, reqs=reqs)
     gpu, _ = _full_check(inp, ell, reqs=reqs, drf_stats=_draft_stats(full, g))
     assert np.all(to_np(gpu["status"]) == 0)
+
+
+def _lazy_check(inp, ell, reqs=None, ell_dev=None, **kw):
+    """Verification that stops at each request's first rejection against the
+    oracle that reads positions in order; statistics of the rows the oracle
+    examined."""
+    ell = np.asarray(ell, np.int64)
+    if ell_dev is None:
+        ell_dev = torch.as_tensor(ell, dtype=torch.int32, device="cuda")
+    gpu = _gpu_verify(inp, ell_dev, alpha=False, stop_at_rejection=True, **kw)
+    reqs = list(range(inp["R"])) if reqs is None else list(reqs)
+    ora = oracle_verify_subset(inp, reqs, ell, stop_at_rejection=True)
+    n_dec, n_near, mism = compare_verify(gpu, ora, reqs)
+    check_examined_stats(gpu, ora, reqs, ell, inp["gmax"])
+    print(f"decisions={n_dec} near-boundary={n_near} diverged={mism}")
+    assert mism <= max(1, 1e-4 * n_dec)
+    return gpu, ora
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_verify_stop_at_rejection_workloads(name):
+    """Same lengths and tokens as reading every row (usable rows), and the
+    oracle's in-order procedure agrees; full block and early-stop lengths."""
+    inp = _to_cuda(verify_config(name, device="cpu"))
+    R, g = inp["R"], inp["gmax"]
+    ref = OS.schedule(to_np(inp["conf"]), to_np(inp["sps"]), OS.EARLY_STOP)
+    for ell in (np.full(R, g), ref["ell"]):
+        gpu, _ = _lazy_check(inp, ell)
+        full = _gpu_verify(inp, torch.as_tensor(ell, dtype=torch.int32, device="cuda"), alpha=False)
+        for k in ("n_acc", "tokens", "status"):
+            assert torch.equal(gpu[k], full[k]), k
+
+
+def test_verify_stop_at_rejection_ragged_and_long_chains():
+    """Ragged vocabulary, padded rows, fp32 and bf16; gamma_max = 255 with
+    drafts close to the targets, so that the eight rounds of positions
+    (2, 6, 14, ..., 256) are all used; gamma_max = 0."""
+    for dtype in (torch.float32, torch.bfloat16):
+        inp = _to_cuda(verify_inputs(R=7, gmax=5, V=40008, ld=40016, dtype=dtype, sigma_t=2.0,
+                                     zipf=True, sigma_d=(0.3, 2.0), seed=77))
+        _lazy_check(inp, [0, 1, 2, 3, 4, 5, 5])
+    inp = _to_cuda(verify_inputs(R=3, gmax=255, V=1024, dtype=torch.bfloat16, sigma_t=2.0,
+                                 sigma_d=(0.02, 0.05), seed=84))
+    _, ora = _lazy_check(inp, [255, 100, 0])
+    assert int(ora["n_acc"].max()) > 30
+    inp = _to_cuda(verify_inputs(R=6, gmax=0, V=5000, dtype=torch.bfloat16, sigma_t=2.0, zipf=True, seed=83))
+    _lazy_check(inp, np.zeros(6))
+
+
+def test_verify_stop_at_rejection_vocab_past_the_lds_block_sums():
+    inp = _to_cuda(verify_inputs(R=2, gmax=2, V=4_000_008, dtype=torch.bfloat16, sigma_t=2.0, zipf=True,
+                                 sigma_d=(1.0, 3.0), seed=85))
+    _lazy_check(inp, [2, 2])
+
+
+def test_verify_stop_at_rejection_ignores_rows_past_the_rejection():
+    """Rows past each request's first rejection spoiled with NaN / -inf: the
+    result is that of the clean rows (reading every row fails those
+    requests); an unusable row at the rejected position, or an unusable bonus
+    row after full acceptance, fails the request."""
+    V, g, R = 4096, 6, 12
+    inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=torch.float32, sigma_t=2.0, sigma_d=(0.5, 2.5),
+                                 seed=90))
+    ell = np.array([6, 6, 6, 5, 6, 4, 6, 6, 3, 6, 6, 2])
+    clean, _ = _lazy_check(inp, ell)
+    n_acc = to_np(clean["n_acc"])
+    tgt, drf = inp["tgt"], inp["drf"]
+    spoiled = []
+    for r in range(R):
+        n, L = int(n_acc[r]), int(ell[r])
+        if n < L - 1:                                  # rows past position n + 1 exist
+            tgt[r * (g + 1) + n + 1:r * (g + 1) + L + 1] = float("nan")
+            drf[r * g + n + 1:r * g + L] = float("-inf")
+            spoiled.append(r)
+    assert len(spoiled) >= 3
+    gpu, _ = _lazy_check(inp, ell)
+    for k in ("n_acc", "tokens", "status"):
+        assert torch.equal(gpu[k], clean[k]), k
+    full = _gpu_verify(inp, torch.as_tensor(ell, dtype=torch.int32, device="cuda"), alpha=False)
+    assert all(to_np(full["status"])[r] & sdv.SD_ST_NONFINITE for r in spoiled)
+    # an unusable row at the rejected position, and an unusable bonus row
+    r = spoiled[0]
+    inp["tgt"][r * (g + 1) + int(n_acc[r]), 0] = float("nan")
+    acc = [q for q in range(R) if n_acc[q] == ell[q]]
+    if acc:
+        inp["tgt"][acc[0] * (g + 1) + int(ell[acc[0]])] = float("-inf")
+    gpu, _ = _lazy_check(inp, ell)
+    st = to_np(gpu["status"])
+    assert st[r] == sdv.SD_ST_NONFINITE
+    if acc:
+        assert st[acc[0]] == sdv.SD_ST_ZERO_Z
+
+
+def test_verify_headline_stop_at_rejection_sampled():
+    """The headline block (R=256, gamma=11, V=151936 bf16), reading rows in
+    rounds; with and without the drafter's statistics."""
+    inp = verify_config("headline", device="cuda")
+    R, g = inp["R"], inp["gmax"]
+    ell = np.full(R, g)
+    reqs = [0, 3, 64, 131, 255]
+    full = _gpu_verify(inp, torch.as_tensor(ell, dtype=torch.int32, device="cuda"), alpha=False)
+    gpu, _ = _lazy_check(inp, ell, reqs=reqs)
+    for k in ("n_acc", "tokens", "status"):
+        assert torch.equal(gpu[k], full[k]), k
+    ds = _draft_stats(full, g)
+    gpu2, _ = _lazy_check(inp, ell, reqs=reqs, drf_stats=ds)
+    for k in ("n_acc", "tokens", "status"):
+        assert torch.equal(gpu2[k], full[k]), k
