@@ -573,7 +573,7 @@ def main():
             "with_drafter_stats_us_per_step": round(lazy[True][0], 1),
             "tokens_same_as_full_pass": lazy[False][1] and lazy[True][1],
             "what": "the same step with SD_VERIFY_STOP_AT_REJECTION: each request's rows are read "
-                    "in rounds of positions (up to 2, 6, 12) and no longer once it is decided, as "
+                    "in rounds of positions (up to 2, 6, then all 11) and no longer once it is decided, as "
                     "nothing after the first rejection can change the outcome; not the headline "
                     "value, which reads every row"},
     }
