@@ -65,6 +65,35 @@ def test_schedule_and_verify_step_replays():
     _replay_and_compare(graph, outs, ref)
 
 
+def test_verify_in_rounds_replays():
+    """Verification that stops at the first rejection (rounds of positions,
+    request lists and counters in the workspace, cleared by the kernels
+    themselves), with the draft rows' (m, Z) supplied: every replay equals
+    the eager call."""
+    inp = verify_config("mid", device="cuda")
+    R, g, V = inp["R"], inp["gmax"], inp["V"]
+    dev = "cuda"
+    ell = torch.full((R,), g, dtype=torch.int32, device=dev)
+    full = sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"], ell,
+                         V, inp["temperature"], inp["seed"], stats=True)
+    ds = full["row_stats"][:, g + 1:, :].contiguous()
+    vo = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+              tokens=torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+              status=torch.empty(R, dtype=torch.int32, device=dev))
+    vws = torch.empty(sdv.sd_verify_workspace_size(R, g, V), dtype=torch.uint8, device=dev)
+
+    def call():
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"], ell, V,
+                      inp["temperature"], inp["seed"], workspace=vws, out=vo, drf_stats=ds,
+                      stop_at_rejection=True)
+
+    call()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in vo.items()}
+    graph = _capture(call)
+    _replay_and_compare(graph, vo, ref)
+
+
 def test_markov_draft_replays():
     inp = markov_inputs(R=16, gamma=5, V=4096, rank=64, H=64, rank_e=32, seed=91, device="cuda")
     R, g, V, rank = inp["R"], inp["gamma"], inp["V"], inp["rank"]

@@ -197,9 +197,9 @@ def test_markov_schedule_and_verify_pipeline(workload):
     d0 = torch.arange(R, dtype=torch.int32, device="cuda") * gamma
     drf = out["q_logits"].view(R * gamma, V)
 
-    def verify(ell_dev):
+    def verify(ell_dev, lazy=False):
         res = sdv.sd_verify(tgt, t0, drf, d0, out["tokens"], ell_dev, V, 1.0, inp["seed"] + 1, probe=True,
-                            stats=True, drf_stats=out["q_stats"])
+                            stats=True, drf_stats=out["q_stats"], stop_at_rejection=lazy)
         torch.cuda.synchronize()
         return res
 
@@ -221,9 +221,11 @@ def test_markov_schedule_and_verify_pipeline(workload):
     reqs = [r for r in SAMPLED if r not in gone]
     assert len(reqs) >= 2
     tgt_h = to_np(tgt.view(R, gamma + 1, V)[reqs]).astype(np.float64)
-    # the oracle's scheduled lengths, then the whole block (more accept tests)
-    for name, ell in (("scheduled", ref_s["ell"]), ("whole block", np.full(R, gamma))):
-        gpu = verify(torch.as_tensor(ell, dtype=torch.int32, device="cuda"))
+    # the oracle's scheduled lengths, then the whole block (more accept
+    # tests), read in one pass and in rounds stopping at the first rejection
+    for name, ell, lazy in (("scheduled", ref_s["ell"], False), ("whole block", np.full(R, gamma), False),
+                            ("whole block, in rounds", np.full(R, gamma), True)):
+        gpu = verify(torch.as_tensor(ell, dtype=torch.int32, device="cuda"), lazy)
         tr0, dr0, tgt_rows, drf_rows = [], [], [], []
         for n, r in enumerate(reqs):
             L = int(ell[r])
@@ -231,13 +233,15 @@ def test_markov_schedule_and_verify_pipeline(workload):
             tgt_rows.extend(tgt_h[n, :L + 1])
             dr0.append(len(drf_rows))
             drf_rows.extend(ref["rows"][r, j].astype(np.float64) for j in range(L))   # the oracle's own rows
-        ora = OV.verify(np.array(tgt_rows), np.array(tr0),
-                        np.array(drf_rows) if drf_rows else np.zeros((1, V)), np.array(dr0),
-                        ref["tokens"][reqs], ell[reqs], V, 1.0, inp["seed"] + 1, req_ids=reqs)
+        fn = OV.verify_until_rejection if lazy else OV.verify
+        ora = fn(np.array(tgt_rows), np.array(tr0), np.array(drf_rows) if drf_rows else np.zeros((1, V)),
+                 np.array(dr0), ref["tokens"][reqs], ell[reqs], V, 1.0, inp["seed"] + 1, req_ids=reqs)
         n_dec, n_near, mism = compare_verify(gpu, ora, reqs)
         print(f"{name}: rows gpu={R + int(ell_g.sum())} oracle={ref_s['B']}; verify decisions={n_dec} "
               f"near-boundary={n_near} diverged={mism}")
         assert mism <= 1
+        if lazy:   # the rows read depend on the decisions; those are compared above
+            continue
         check_stats(gpu, ora, reqs, ell, gamma, draft=False)
         rs = to_np(gpu["row_stats"])
         for r in reqs:   # the draft slots report the head's (m, Z) of its own rows
