@@ -28,8 +28,9 @@
 // Verification that stops at each request's first rejection runs the
 // bandwidth pass and the deciding half of k_finish in rounds of positions
 // (up to 2, 6, 14, ...): a round decides the requests that rejected, failed
-// or reached their bonus row and lists the others for the next round; then
-// one k_finish launch makes every recorded draw at once.
+// or reached their bonus row and lists the others for the next round; the
+// last round's k_finish decides the requests still listed and makes every
+// draw at once.
 //   k_alpha_sums,   only when the acceptance rates are asked for: sums of
 //   k_alpha_total   min(p, q) per (request, position, chunk), then per row -
 //                   the probability that the position is accepted, which is
@@ -63,7 +64,8 @@ static_assert(SD_MAX_GAMMA < kFinThreads, "one accept test per thread");
 
 // The correction draw a request was decided on.
 struct DrawRec {
-  int kind;              // 0: nothing to draw (the request failed), 1: residual, 2: target row
+  int kind;              // 0: nothing to draw (the request failed), 1: residual, 2: target row,
+                         // 3: not decided yet (listed for the next round)
   int n;                 // drafts accepted
   int st;                // status bits so far
   int pos;               // position of the drawn token
@@ -200,11 +202,11 @@ __device__ __forceinline__ double block_incl_scan(double v, int lane, int wave, 
 
 // ---------------------------------------------------------------------------
 // Request r, up to its correction draw: the rows' (m, Z), the accept tests
-// and the decision.  Returns true with the draw to make in *rec; false when
-// the request failed (its outputs written) or is not decided yet (listed for
-// the next round).
+// and the decision, recorded in *rec: the draw to make (kind 1 or 2), a
+// failure (kind 0, its outputs written) or no decision yet (kind 3, listed
+// for the next round).
 template <bool BF16>
-__device__ __forceinline__ bool finish_decide(const VerifyArgs& a, int r, DrawRec* rec) {
+__device__ __forceinline__ void finish_decide(const VerifyArgs& a, int r, DrawRec* rec) {
   using VT = sdv::Vec<BF16>;
   __shared__ float sRef[kMaxSlots];
   __shared__ double sZ[kMaxSlots];
@@ -327,7 +329,8 @@ __device__ __forceinline__ bool finish_decide(const VerifyArgs& a, int r, DrawRe
   };
   if (s_st) {  // a needed row is unusable
     fail(s_st);
-    return false;
+    rec->kind = 0;
+    return;
   }
   const int jb = s_jb;  // kNone unless rows past the first rejection are not needed
 
@@ -363,11 +366,13 @@ __device__ __forceinline__ bool finish_decide(const VerifyArgs& a, int r, DrawRe
   const bool rejected = jstar <= Lt;
   if (jb != kNone && !rejected) {  // an unusable row before any rejection
     fail(s_rst[jb - 1] | (jb <= gmax ? s_rst[gmax + jb] : 0));
-    return false;
+    rec->kind = 0;
+    return;
   }
   if (!rejected && L >= a.cover) {  // all accepted so far; the rest is not read yet
     if (tid == 0) a.next_list[atomicAdd(a.next_count, 1)] = r;
-    return false;
+    rec->kind = 3;
+    return;
   }
   const int n = rejected ? jstar - 1 : L;
   for (int t = tid; t <= gmax; t += kFinThreads) out_tok[t] = (t < n) ? drafts[t] : -1;
@@ -387,7 +392,6 @@ __device__ __forceinline__ bool finish_decide(const VerifyArgs& a, int r, DrawRe
   rec->izt = (float)(1.0 / sZ[pos - 1]);
   rec->mcd = rejected ? sRef[gmax + jstar] : 0.0f;
   rec->izd = rejected ? (float)(1.0 / sZ[gmax + jstar]) : 1.0f;
-  return true;
 }
 
 // The correction draw of request r (every thread of the workgroup): the
@@ -622,32 +626,29 @@ __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec 
 }
 
 // The finishing kernel, one workgroup per request: decide and draw at once
-// (every row read in one pass), or in rounds: decide only (the draws
-// recorded), then every recorded draw at once.
-enum { kFused = 0, kDecide = 1, kDraw = 2 };
+// (every row read in one pass), or in rounds: decide only, recording the
+// draws, in every round but the last; the last decides the requests still
+// listed and makes every draw at once.
+enum { kFused = 0, kDecide = 1, kFinal = 2 };
 
 template <bool BF16, int PHASE>
 __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   DrawRec rec;
   int r;
-  if constexpr (PHASE == kDraw) {
+  if constexpr (PHASE == kFinal) {
     r = (int)blockIdx.x;
     rec = a.recs[r];
-    if (rec.kind == 0) return;  // failed: outputs already written
+    if (rec.kind == 3) finish_decide<BF16>(a, r, &rec);  // listed for this round
   } else {
     if (a.list && (int)blockIdx.x >= *a.count) return;
     r = a.list ? a.list[blockIdx.x] : (int)blockIdx.x;
-    const bool draw = finish_decide<BF16>(a, r, &rec);
+    finish_decide<BF16>(a, r, &rec);
     if constexpr (PHASE == kDecide) {
-      if (threadIdx.x == 0) {
-        if (!draw) rec.kind = 0;  // failed, or decided in a later round
-        a.recs[r] = rec;
-      }
+      if (threadIdx.x == 0) a.recs[r] = rec;
       return;
     }
-    if (!draw) return;
   }
-  finish_draw<BF16>(a, r, rec);
+  if (rec.kind == 1 || rec.kind == 2) finish_draw<BF16>(a, r, rec);
 }
 
 // ---------------------------------------------------------------------------
@@ -874,8 +875,9 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   // Rounds of positions: round k reads target slots [prev, cover) and draft
   // positions (prev, cover] of the requests still undecided (every request
   // in round 0), then decides those that rejected, failed, or reached their
-  // bonus row, and lists the others for round k + 1.  The draws of all
-  // requests then run at once.
+  // bonus row, and lists the others for round k + 1.  The last round decides
+  // the requests still listed and makes the draws of all at once (with one
+  // round, the one-pass kernel).
   int prev = 0;
   for (int k = 0; prev < gamma_max + 1; ++k) {
     const int cover = std::min(next_cover(prev), gamma_max + 1);
@@ -894,12 +896,15 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
     a.count = ra.count;
     a.next_list = last ? nullptr : lists + (size_t)(k + 1) * R;
     a.next_count = last ? nullptr : counts + k + 1;
-    const int rc =
-        bf16 ? launch_finish<true, kDecide>(stream, R, a) : launch_finish<false, kDecide>(stream, R, a);
+    int rc;
+    if (!last)
+      rc = bf16 ? launch_finish<true, kDecide>(stream, R, a) : launch_finish<false, kDecide>(stream, R, a);
+    else if (k == 0)
+      rc = bf16 ? launch_finish<true, kFused>(stream, R, a) : launch_finish<false, kFused>(stream, R, a);
+    else
+      rc = bf16 ? launch_finish<true, kFinal>(stream, R, a) : launch_finish<false, kFinal>(stream, R, a);
     if (rc != SD_OK) return rc;
     prev = cover;
   }
-  a.list = nullptr;
-  a.count = nullptr;
-  return bf16 ? launch_finish<true, kDraw>(stream, R, a) : launch_finish<false, kDraw>(stream, R, a);
+  return SD_OK;
 }

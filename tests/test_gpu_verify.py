@@ -168,6 +168,10 @@ def test_verify_ragged_async_sampled():
     assert np.array_equal(to_np(sched["ell"]), ref["ell"])
     gpu, _ = _full_check(inp, ref["ell"], reqs=[0, 3, 99, 256, 400, 511], ell_dev=sched["ell"])
     assert np.all(to_np(gpu["status"]) == 0)   # no NaN slot was read
+    # the same step read in rounds, stopping at each request's first rejection
+    lazy, _ = _lazy_check(inp, ref["ell"], reqs=[0, 7, 300, 511], ell_dev=sched["ell"])
+    for k in ("n_acc", "tokens", "status"):
+        assert torch.equal(lazy[k], gpu[k]), k
 
 
 def test_verify_degenerate_rows_and_tokens():
