@@ -196,7 +196,7 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *               positions 1..gamma_max+1, slots gamma_max+1.. are draft rows of
  *               positions 1..gamma_max; only slots inside the batch are written
  *               (draft slots copy drf_stats when it is given).  An all -inf
- *               row reports (-inf, 0).
+ *               row reports (-inf, 0).  8-byte aligned.
  *   accept_prob [R][gamma_max] fp32 or NULL: alpha_j = sum_v min(p_j(v), q_j(v)),
  *               the probability that position j is accepted given the prefix
  *               was, i.e. 1 - TV(p_j, q_j), the label the confidence head is
@@ -207,7 +207,8 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *             rejection is discarded [SD 1.1], so the rows past it cannot
  *             change the outcome; with this option each request's rows are
  *             read in rounds of positions (up to 2, 6, 14, ...) and a request
- *             stops being read once it is decided.  On usable rows the
+ *             stops being read once it is decided (the request lists and the
+ *             recorded draws live in the workspace).  On usable rows the
  *             result is the same; a row past the first rejection is never
  *             read, so it fails nothing (a position fails the request only
  *             when its own target or draft row is unusable, the bonus row
@@ -223,8 +224,9 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  * tested position sets BAD_TOKEN and counts as a rejection; a needed row with
  * NaN / +inf (NONFINITE) or all -inf (ZERO_Z) fails the request: n_accepted 0
  * and every output token -1 (every batch row is needed, or under
- * SD_VERIFY_STOP_AT_REJECTION the rows up to the first rejection); an empty residual sets ZERO_RESIDUAL and the
- * token is drawn from p_j*; q(x) = 0 sets ZERO_Q (accepted iff p(x) > 0).
+ * SD_VERIFY_STOP_AT_REJECTION the rows up to the first rejection); an empty
+ * residual sets ZERO_RESIDUAL and the token is drawn from p_j*; q(x) = 0
+ * sets ZERO_Q (accepted iff p(x) > 0).
  */
 size_t sd_verify_workspace_size(int R, int gamma_max, int V);
 int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype,
