@@ -240,7 +240,7 @@ def bench_rnn(sdv, torch, steps):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     hbm = (2 * g * V * d + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # C per step + U + L + h
-    flops = 2.0 * R * (2 * d) * V * g                                      # two bf16 terms of the state
+    flops = 2.0 * R * (3 * d) * V * g                                      # three bf16 terms of the state
     return {"workload": f"R={R}, gamma={g}, V={V}, d={d}, H=4096, bf16",
             "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
             "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,

@@ -77,10 +77,11 @@ __global__ __launch_bounds__(kThreads) void k_hidden_dot(const uint16_t* __restr
 // v_mfma_f32_16x16x32_bf16, fused with + U_k, the bf16 rounding, the q_logits
 // store and one partial (max, sum 2^(L*c - ref)) per (request, 128-column
 // tile).  NSPLIT = 1, the Markov head: row r of A is A_k[x_{k-1}], gathered
-// from the table at the start (zeros for an invalid token).  NSPLIT = 2, the
-// RNN head: Ag[r] holds the state as two bf16 terms, hi = bf16(s) then
-// lo = bf16(s - hi), both multiplied by the same C fragments, so the product
-// carries the fp32 state to within 2^-17 of each element.
+// from the table at the start (zeros for an invalid token).  NSPLIT = 3, the
+// RNN head: Ag[r] holds the state as three bf16 terms, hi = bf16(s),
+// mid = bf16(s - hi), lo = bf16(s - hi - mid), all multiplied by the same C
+// fragments; each term holds the next 8 bits of the fp32 significand, so the
+// three carry the state exactly (normal values).
 //
 // The loads are pipelined by specialised waves.  One workgroup per CU walks
 // the 128-column tiles t = blockIdx.x, + gridDim.x, ... (so that at any time
@@ -138,6 +139,11 @@ __device__ __forceinline__ int c_swz(int row, int cpr) {
   const int p2 = cpr & -cpr;
   return row & ((p2 < 16 ? p2 : 16) - 1);
 }
+
+// 32-element K slices of the A rows a compute wave keeps: rank <= kMaxRank
+// (Markov), state d <= kMaxRank / 2 (RNN).
+template <int NSPLIT>
+constexpr int kHeadKs = NSPLIT == 1 ? kMaxRank / 32 : kMaxRank / 64;
 
 template <int NSPLIT>
 __global__ __launch_bounds__(kWsThreads) void k_head_bias(
@@ -207,19 +213,20 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
   const int r = m0 + req;
   const bool rvalid = r < R;
   const size_t urow = ((size_t)(rvalid ? r : 0) * gamma + (k - 1)) * V;
-  uint4 agf[NSPLIT][kMaxRank / 32];
+  constexpr int kKs = kHeadKs<NSPLIT>;
+  uint4 agf[NSPLIT][kKs];
   if (A != nullptr) {  // Markov: gather A_k[x_{k-1}] here, under the first stage's load
     const int x = rvalid ? (k == 1 ? x0[r] : tokens[(size_t)r * gamma + (k - 2)]) : -1;
     const bool xv = x >= 0 && x < V;  // no bias for an invalid token
     const uint16_t* arow = A + ((size_t)(k - 1) * V + (xv ? x : 0)) * kdim;
 #pragma unroll
-    for (int ks = 0; ks < kMaxRank / 32; ++ks)
+    for (int ks = 0; ks < kKs; ++ks)
       agf[0][ks] = (xv && ks < kb) ? *(const uint4*)(arow + ks * 32 + q * 8) : make_uint4(0, 0, 0, 0);
   } else {
 #pragma unroll
     for (int sp = 0; sp < NSPLIT; ++sp)
 #pragma unroll
-      for (int ks = 0; ks < kMaxRank / 32; ++ks)
+      for (int ks = 0; ks < kKs; ++ks)
         agf[sp][ks] = (rvalid && ks < kb)
                           ? *(const uint4*)(Ag + (size_t)r * NSPLIT * kdim + (sp * kb + ks) * 32 + q * 8)
                           : make_uint4(0, 0, 0, 0);
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kMaxRank / 32; ++ks) {
+    for (int ks = 0; ks < kKs; ++ks) {
       if (ks < kb) {
         uint4 a[4];  // the four row blocks' fragments, read together
 #pragma unroll
@@ -313,7 +320,7 @@ struct NextRows {
   const uint16_t* W;        // W [d][d]
   const uint16_t* Es;       // E_s [V][d]
   float* state;             // [R][d]
-  uint16_t* Ag;             // [R][2d]: the state as two bf16 terms
+  uint16_t* Ag;             // [R][3d]: the state as three bf16 terms
 };
 
 // RNN: row o = threadIdx.x of W times the state s_k in LDS (0 for o >= d).
@@ -334,9 +341,21 @@ __device__ float rnn_w_times_state(const NextRows& nr, const float* s_s) {
   return acc;
 }
 
+// Element o of a state as the three bf16 terms the bias kernel multiplies:
+// hi = bf16(s), mid = bf16(s - hi), lo = bf16(s - hi - mid) at row offsets
+// 0, d and 2d (each subtraction is exact in fp32).
+__device__ __forceinline__ void split_state(uint16_t* row, int d, int o, float s) {
+  const uint16_t hi = sdv::f32_to_bf16_rne(s);
+  const float r1 = s - sdv::bf16_to_f32(hi);
+  const uint16_t mid = sdv::f32_to_bf16_rne(r1);
+  row[o] = hi;
+  row[d + o] = mid;
+  row[2 * d + o] = sdv::f32_to_bf16_rne(r1 - sdv::bf16_to_f32(mid));
+}
+
 // RNN, once x_k is known: s_{k+1} = tanh(W s_k + E_s[x_k]) in fp32 (no
 // embedding term for an invalid token), kept in state[r] and written to Ag[r]
-// as its two bf16 terms; ws = (W s_k)[threadIdx.x].
+// as its three bf16 terms; ws = (W s_k)[threadIdx.x].
 __device__ void rnn_next_state(const NextRows& nr, int r, int V, int tok, float ws) {
   const int d = nr.rank, o = threadIdx.x;  // d <= kThreads
   if (o < d) {
@@ -344,9 +363,7 @@ __device__ void rnn_next_state(const NextRows& nr, int r, int V, int tok, float 
     if (tok >= 0 && tok < V) acc += sdv::bf16_to_f32(nr.Es[(size_t)tok * d + o]);
     const float sn = tanhf(acc);
     nr.state[(size_t)r * d + o] = sn;
-    const uint16_t hi = sdv::f32_to_bf16_rne(sn);
-    nr.Ag[(size_t)r * 2 * d + o] = hi;
-    nr.Ag[(size_t)r * 2 * d + d + o] = sdv::f32_to_bf16_rne(sn - sdv::bf16_to_f32(hi));
+    split_state(nr.Ag + (size_t)r * 3 * d, d, o, sn);
   }
 }
 
@@ -549,14 +566,12 @@ __global__ __launch_bounds__(kThreads) void k_rnn_init(int R, int V, int d, cons
   for (int o = threadIdx.x; o < d; o += kThreads) {
     const float sn = tanhf(valid ? sdv::bf16_to_f32(Es[(size_t)x * d + o]) : 0.0f);
     state[(size_t)r * d + o] = sn;
-    const uint16_t hi = sdv::f32_to_bf16_rne(sn);
-    Ag[(size_t)r * 2 * d + o] = hi;
-    Ag[(size_t)r * 2 * d + d + o] = sdv::f32_to_bf16_rne(sn - sdv::bf16_to_f32(hi));
+    split_state(Ag + (size_t)r * 3 * d, d, o, sn);
   }
 }
 
 // Workspace: hdot [R][gamma] fp32, tile partials [R][n_tiles] float2, and for
-// the RNN head the split state [R][arow = 2d] bf16 and the state [R][d] fp32.
+// the RNN head the split state [R][arow = 3d] bf16 and the state [R][d] fp32.
 size_t head_ws_bytes(int R, int gamma, int V, int arow, int d) {
   const size_t n_tiles = ((size_t)V + kTileN - 1) / kTileN;
   return sdv_align256((size_t)R * gamma * sizeof(float)) +
@@ -565,7 +580,7 @@ size_t head_ws_bytes(int R, int gamma, int V, int arow, int d) {
          sdv_align256((size_t)R * d * sizeof(float));
 }
 size_t markov_ws_bytes(int R, int gamma, int V, int) { return head_ws_bytes(R, gamma, V, 0, 0); }
-size_t rnn_ws_bytes(int R, int gamma, int V, int d) { return head_ws_bytes(R, gamma, V, 2 * d, d); }
+size_t rnn_ws_bytes(int R, int gamma, int V, int d) { return head_ws_bytes(R, gamma, V, 3 * d, d); }
 
 // Checks shared by both heads (everything but the head's own tables).
 int check_head_args(int R, int gamma, int V, int H, int rank_e, float temperature) {
@@ -597,7 +612,7 @@ int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_st
     SDV_TRY_LAUNCH(sdv::launch(k_head_bias<NSPLIT>, grid_bias, dim3(kWsThreads), kWsLds, stream, R,
                                gamma, k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag, A, x0,
                                (const int32_t*)tokens, q_logits, partial, n_tiles));
-    SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT == 2>, dim3(R), dim3(kThreads), 0, stream, gamma,
+    SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT != 1>, dim3(R), dim3(kThreads), 0, stream, gamma,
                                k, V, H, rank_e, c, inv_t, seed, pos0, x0, E, w, hdot,
                                (const float2*)partial, n_tiles, (const uint16_t*)q_logits, nr, tokens,
                                (float2*)q_stats, conf, status));
@@ -682,7 +697,7 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
   float2* partial = (float2*)p;
   p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
   uint16_t* Ag = (uint16_t*)p;
-  p += sdv_align256((size_t)R * 2 * d * sizeof(uint16_t));
+  p += sdv_align256((size_t)R * 3 * d * sizeof(uint16_t));
   const NextRows nr{d, W, Es, (float*)p, Ag};
 
   const int rows = R * gamma;
@@ -690,6 +705,6 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
                              rows, hdot));
   SDV_TRY_LAUNCH(sdv::launch(k_rnn_init, dim3(R), dim3(kThreads), 0, stream, R, V, d, Es, x0, nr.state,
                              nr.Ag));
-  return run_head<2>(stream, R, gamma, V, d, 0, temperature, seed, pos0, U, nullptr, Ct, x0, H, E,
+  return run_head<3>(stream, R, gamma, V, d, 0, temperature, seed, pos0, U, nullptr, Ct, x0, H, E,
                      rank_e, w, hdot, partial, nr, tokens, q_logits, q_stats, conf, status);
 }

@@ -289,8 +289,8 @@ int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
  *   L_k = bf16_rne( U[r][k-1] + s_k . C )     (C shared across positions)
  * with x_k, conf and the degenerate cases exactly as sd_markov_draft (an
  * anchor or token outside [0, V) contributes no embedding term).  The state
- * enters the MFMA product as two bf16 terms (hi = bf16(s), lo = bf16(s - hi)),
- * so each state element is carried to within 2^-17 of its fp32 value.
+ * enters the MFMA product as three bf16 terms (hi = bf16(s), mid = bf16(s -
+ * hi), lo = bf16(s - hi - mid)), which carry its fp32 value exactly.
  *   d % 32 == 0, 32 <= d <= 128; other limits as sd_markov_draft
  *   W  [d][d] bf16 (row o: weights of output o);  Es [V][d] bf16
  *   Ct [V][d] bf16: row n is column n of C

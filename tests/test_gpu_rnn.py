@@ -5,7 +5,7 @@ included) from the same seeded inputs; no GPU output enters it.  Along the
 history the two chains share, each GPU bf16 logit must be a round-to-nearest
 of a value within 1e-5 * sum|s_i C_i| + 1e-5 * sum|C_i| + 1e-7 * |y| of the
 oracle's exact y = U + s . C (fp64; the middle term bounds the fp32 state's
-error, the two-term bf16 split included); the confidence and the row's
+error; its three bf16 terms carry it exactly); the confidence and the row's
 (m, Z) must match within 1e-5 relative; tokens must be equal except where
 the oracle's draw is near-boundary, where the chains may part and the rest of
 that request is not compared.
