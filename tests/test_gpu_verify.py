@@ -118,6 +118,22 @@ def test_verify_temperature_and_positions():
     _full_check(inp, np.full(9, 6))
 
 
+@pytest.mark.parametrize("T", [0.05, 4.0])
+def test_verify_low_and_high_temperature(T):
+    """T = 0.05 (rows nearly one-hot: logits / T span hundreds of units, the
+    exponentials of everything but the top few underflow) and T = 4 (rows
+    nearly flat); drafts drawn at the same temperature; in one pass and in
+    rounds."""
+    for dtype in (torch.bfloat16, torch.float32):
+        inp = _to_cuda(verify_inputs(R=8, gmax=5, V=30000, dtype=dtype, sigma_t=2.5, zipf=True,
+                                     sigma_d=(0.2, 2.0), seed=91, temperature=T))
+        ell = np.array([5, 5, 4, 5, 3, 5, 5, 1])
+        full, _ = _full_check(inp, ell)
+        lazy, _ = _lazy_check(inp, ell)
+        for k in ("n_acc", "tokens", "status"):
+            assert torch.equal(lazy[k], full[k]), k
+
+
 def test_verify_packed_layout():
     # rows of consecutive requests packed back to back (no reserved slots)
     inp = _to_cuda(verify_inputs(R=6, gmax=4, V=4096, dtype=torch.bfloat16, sigma_t=2.0,
