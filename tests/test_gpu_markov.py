@@ -113,6 +113,19 @@ def test_markov_small_full():
     assert parted <= partings_bound(compared)
 
 
+@pytest.mark.parametrize("T", [0.6, 2.0])
+def test_markov_temperature(T):
+    """Drafting at T != 1: logits divided by T before the draw; the rows'
+    (m, Z) reported at that temperature."""
+    inp = markov_inputs(R=6, gamma=4, V=3000, rank=64, H=32, rank_e=16, sigma_u=2.0, sigma_f=0.3,
+                        seed=95, device="cuda")
+    inp["temperature"] = T
+    out = _run(inp)
+    ref = oracle_chain(inp, range(6), keep=range(6))
+    compared, parted, _ = check_chain(inp, out, ref, range(6))
+    assert parted <= partings_bound(compared)
+
+
 def test_markov_whole_block_matches_the_oracle_draft():
     """The oracle's whole-block entry point (markov_draft) on the same inputs:
     tokens equal up to a near-boundary parting, statuses equal."""

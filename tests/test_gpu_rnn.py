@@ -116,6 +116,17 @@ def test_rnn_state_sizes_and_positions(d):
     assert parted <= partings_bound(compared)
 
 
+@pytest.mark.parametrize("T", [0.6, 2.0])
+def test_rnn_temperature(T):
+    """Drafting at T != 1, as for the Markov head."""
+    inp = rnn_inputs(R=6, gamma=4, V=3000, d=64, H=32, rank_e=16, sigma_c=0.3, seed=101, device="cuda")
+    inp["temperature"] = T
+    out = _run(inp)
+    ref = oracle_chain(inp, range(6), keep=range(6))
+    compared, parted, _ = check_chain(inp, out, ref, range(6))
+    assert parted <= partings_bound(compared)
+
+
 def test_rnn_whole_block_matches_the_oracle_draft():
     """The oracle's whole-block entry point (rnn_draft) on the same inputs:
     tokens equal up to a near-boundary parting, statuses equal."""
