@@ -113,6 +113,19 @@ def test_markov_small_full():
     assert parted <= partings_bound(compared)
 
 
+@pytest.mark.parametrize("rank", [96, 160, 224])
+def test_markov_ranks_off_the_powers_of_two(rank):
+    """rank = 32 * 3, 5, 7: C rows of 12, 20, 28 sixteen-byte chunks (the LDS
+    swizzle groups by the largest power of two dividing that count) and 7,
+    9, 11 copies per loader wave and stage; a ragged last tile (V = 3000)."""
+    inp = markov_inputs(R=5, gamma=3, V=3000, rank=rank, H=32, rank_e=16, sigma_u=2.0, sigma_f=0.2,
+                        seed=96 + rank, device="cuda")
+    out = _run(inp)
+    ref = oracle_chain(inp, range(5), keep=range(5))
+    compared, parted, _ = check_chain(inp, out, ref, range(5))
+    assert parted <= partings_bound(compared)
+
+
 @pytest.mark.parametrize("T", [0.6, 2.0])
 def test_markov_temperature(T):
     """Drafting at T != 1: logits divided by T before the draw; the rows'
