@@ -126,6 +126,17 @@ def test_markov_ranks_off_the_powers_of_two(rank):
     assert parted <= partings_bound(compared)
 
 
+def test_markov_vocab_beyond_1024_tiles():
+    """V = 300000: 2344 column tiles, so each select thread combines a run of
+    ten tile partials (four of them preloaded) before the walk."""
+    inp = markov_inputs(R=3, gamma=2, V=300000, rank=32, H=16, rank_e=8, sigma_u=2.0, sigma_f=0.3,
+                        seed=97, device="cuda")
+    out = _run(inp)
+    ref = oracle_chain(inp, range(3), keep=range(3))
+    compared, parted, _ = check_chain(inp, out, ref, range(3))
+    assert parted <= partings_bound(compared)
+
+
 @pytest.mark.parametrize("T", [0.6, 2.0])
 def test_markov_temperature(T):
     """Drafting at T != 1: logits divided by T before the draw; the rows'
