@@ -27,6 +27,15 @@ def run_smoke():
     ora = oracle_verify_subset(inp, reqs, ref["ell"])
     n_dec, n_near, _ = compare_verify(gpu, ora, reqs)
     check_stats(gpu, ora, reqs, ref["ell"], inp["gmax"])
+    # the same verification in rounds that stop at the first rejection, with
+    # the draft rows' (m, Z) handed over as a drafter would
+    g = inp["gmax"]
+    lazy = sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                         sched["ell"], inp["V"], 1.0, inp["seed"], stop_at_rejection=True,
+                         drf_stats=gpu["row_stats"][:, g + 1:, :].contiguous())
+    torch.cuda.synchronize()
+    ora_l = oracle_verify_subset(inp, reqs, ref["ell"], stop_at_rejection=True)
+    compare_verify(lazy, ora_l, reqs)
 
     m = markov_inputs(R=3, gamma=3, V=1024, rank=32, H=16, rank_e=8, sigma_f=0.3, device=dev)
     out = sdv.sd_markov_draft(m["U"], m["A"], m["Ct"], m["x0"], m["h"], m["E"], m["w"], 1.0, m["seed"])
