@@ -21,6 +21,10 @@
 //                    rescan 128 logits, emit x_k (and, when asked, the row's
 //                    (m, Z), which spares the verifier a pass over the row)
 // plus, up front, one k_hidden_dot launch for w_h . h_k of every position.
+//
+// sd_rnn_draft runs the same loop for the RNN head: k_rnn_init computes s_1,
+// the bias kernel takes the state's three bf16 terms as its A rows against
+// the shared readout C, and the select kernel also advances the state.
 #include <algorithm>
 
 #include "sdv_common.h"
@@ -29,8 +33,8 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileN = 128;  // vocabulary columns per workgroup (4 waves x 32)
-constexpr int kTileM = 128;  // requests per workgroup
+constexpr int kTileN = 128;  // vocabulary columns per tile (two 64-column stages)
+constexpr int kTileM = 128;  // requests per bias workgroup (8 compute waves x 16)
 constexpr int kMaxRank = 256;
 static_assert(kMaxRank / 2 <= kThreads, "an RNN state of d <= kMaxRank / 2: one element per thread");
 constexpr float kNegInf = -__builtin_huge_valf();
