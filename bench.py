@@ -323,6 +323,49 @@ def bench_markov(sdv, torch, steps, hip):
     return res
 
 
+def sweep(sdv, torch, steps):
+    """Verification alone on the headline workload's distributions at other
+    batch sizes (full blocks, gamma = 11, V = 151936 bf16): one pass, and in
+    rounds stopping at each request's first rejection."""
+    from workloads import verify_config
+    from workloads.synth import headline_bytes
+    dev = "cuda"
+    res = []
+    for R in (16, 64, 256, 1024):
+        inp = verify_config("headline", device=dev, R=R)
+        g, V = inp["gmax"], inp["V"]
+        ell = torch.full((R,), g, dtype=torch.int32, device=dev)
+        ws = torch.empty(sdv.sd_verify_workspace_size(R, g, V), dtype=torch.uint8, device=dev)
+        vo = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                  tokens=torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+                  status=torch.empty(R, dtype=torch.int32, device=dev))
+        n = max(5, min(steps, 20))
+        for lazy in (False, True):
+            call = lambda: sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"],
+                                         inp["draft_tokens"], ell, V, inp["temperature"], inp["seed"],
+                                         workspace=ws, out=vo, stop_at_rejection=lazy)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            rows = R * (g + 1)
+            res.append({"R": R, "mode": "in rounds" if lazy else "one pass", "us_per_call": round(us, 1),
+                        "rows_per_s": round(rows / (us / 1e6), 1),
+                        "all_rows_GBps": round(headline_bytes(R, g, V) / (us / 1e6) / 1e9, 1),
+                        "batch_bytes": headline_bytes(R, g, V)})
+            print(json.dumps(res[-1]), file=sys.stderr, flush=True)
+        del inp, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +374,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-markov", action="store_true")
     ap.add_argument("--no-early-stop", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time verification alone at R = 16, 64, 256, 1024 (headline distributions, "
+                         "full blocks), in one pass and in rounds, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device three times (the known-size kernel that "
                          "scales the rocprofv3 byte counters), then exit")
@@ -358,6 +404,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+        return
+    if args.sweep:
+        print(json.dumps({"verify_batch_sweep": sweep(sdv, torch, args.steps)}))
         return
     print("generating inputs", file=sys.stderr, flush=True)
     # three independent input sets of 1.79 GB each, rotated: no step can be
