@@ -214,7 +214,10 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *             when its own target or draft row is unusable, the bonus row
  *             only after full acceptance); row_stats and probe_probs are
  *             written for the rows and positions examined only; accept_prob
- *             must be NULL.
+ *             must be NULL.  Each round adds two launches: on a batch that
+ *             fits the last-level cache (tens of requests at V ~ 150k) the
+ *             one-pass call is faster; from ~64 requests at gamma 11 the
+ *             rounds are (2x at 256-1024 requests on MI355X).
  * prof_start, prof_stop  optional HIP events (both or neither): recorded on
  *             `stream` right before and after the row-statistics pass (the
  *             bandwidth-bound kernel that streams every row once; its first
