@@ -27,7 +27,8 @@
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
  *     stated otherwise.  The library never allocates, frees or synchronises;
  *     all scratch lives in a caller-provided workspace of at least
- *     sd_*_workspace_size() bytes (256-byte aligned).
+ *     sd_*_workspace_size() bytes (256-byte aligned).  Calls that may run at
+ *     the same time (other streams) need workspaces of their own.
  *   - The return value reports host-side argument checks and launch errors
  *     only (SD_OK or a negative SD_E* code).  Nothing is enqueued when an
  *     argument check fails.  Data-dependent faults are reported per request
