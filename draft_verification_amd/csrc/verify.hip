@@ -24,6 +24,10 @@
 //                   u * sum(w) with a workgroup prefix sum, and one wave scans
 //                   that block.  A bonus draw locates its chunk from the first
 //                   pass's partials and rescans only that chunk.
+//   k_draw_sums     small batches only (too few requests to fill the CUs):
+//                   k_finish records the draws, this kernel takes the block
+//                   sums with many workgroups per rejected row pair, and a
+//                   last k_finish launch locates and scans as above
 //
 // Verification that stops at each request's first rejection runs the
 // bandwidth pass and the deciding half of k_finish in rounds of positions
@@ -394,10 +398,31 @@ __device__ __forceinline__ void finish_decide(const VerifyArgs& a, int r, DrawRe
   rec->izd = rejected ? (float)(1.0 / sZ[gmax + jstar]) : 1.0f;
 }
 
+// Per-lane part of one 1024-element block's residual mass, the block's two
+// rows held in registers (lane l holds vectors k*64 + l): fp32 weights, fp64
+// sum.
+template <bool BF16, int VL>
+__device__ __forceinline__ double block_lane_mass(const uint4 (&t)[VL], const uint4 (&d)[VL],
+                                                  const DrawParams& dp) {
+  using VT = sdv::Vec<BF16>;
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < VL; ++k) {
+    float xt[VT::kElems], xd[VT::kElems];
+    VT::unpack(t[k], xt);
+    VT::unpack(d[k], xd);
+#pragma unroll
+    for (int e = 0; e < VT::kElems; ++e)
+      acc += (double)draw_weight(xt[e], xd[e], 1, dp.c, dp.mct, dp.izt, dp.mcd, dp.izd);
+  }
+  return acc;
+}
+
 // The correction draw of request r (every thread of the workgroup): the
 // residual max(0, p - q) of the rejected position or the target row after
 // the last draft, by inverse CDF; writes the token, n_accepted and status.
-template <bool BF16>
+// SUMS_READY: the residual's block sums are already in a.bsum (k_draw_sums).
+template <bool BF16, bool SUMS_READY>
 __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec rec) {
   using VT = sdv::Vec<BF16>;
   constexpr int VL = kBlk / VT::kElems / 64;  // vectors per lane per row of a block
@@ -438,42 +463,35 @@ __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec 
 
   double target = 0.0;
   if (dp.kind == 1) {
-    // Residual mass per block: wave w streams blocks w, w + 16, ... with the
-    // next block's loads issued before the current block is summed.  The
-    // block sums stay in LDS when they fit.
-    double* bs = n_blk <= kLdsBlocks ? s_bs : bsum;
-    uint4 ct[VL], cd[VL];
-    auto load = [&](int b, uint4 (&t)[VL], uint4 (&d)[VL]) {
+    // Residual mass per block (unless k_draw_sums took it): wave w streams
+    // blocks w, w + 16, ... with the next block's loads issued before the
+    // current block is summed.  The block sums stay in LDS when they fit.
+    double* bs = bsum;
+    if constexpr (!SUMS_READY) {
+      if (n_blk <= kLdsBlocks) bs = s_bs;
+      uint4 ct[VL], cd[VL];
+      auto load = [&](int b, uint4 (&t)[VL], uint4 (&d)[VL]) {
 #pragma unroll
-      for (int k = 0; k < VL; ++k) {
-        const int v = b * kBlkVec + k * 64 + lane;  // v < nvec implies b < n_blk
-        t[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
-        d[k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
+        for (int k = 0; k < VL; ++k) {
+          const int v = b * kBlkVec + k * 64 + lane;  // v < nvec implies b < n_blk
+          t[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
+          d[k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
+        }
+      };
+      load(wave, ct, cd);
+      for (int b = wave; b < n_blk; b += kFinWaves) {
+        uint4 nt[VL], nd[VL];
+        load(b + kFinWaves, nt, nd);
+        const double acc = sdv::wave_sum_d(block_lane_mass<BF16, VL>(ct, cd, dp));
+        if (lane == 0) bs[b] = acc;
+#pragma unroll
+        for (int k = 0; k < VL; ++k) {
+          ct[k] = nt[k];
+          cd[k] = nd[k];
+        }
       }
-    };
-    load(wave, ct, cd);
-    for (int b = wave; b < n_blk; b += kFinWaves) {
-      uint4 nt[VL], nd[VL];
-      load(b + kFinWaves, nt, nd);
-      double acc = 0.0;
-#pragma unroll
-      for (int k = 0; k < VL; ++k) {
-        float xt[VT::kElems], xd[VT::kElems];
-        VT::unpack(ct[k], xt);
-        VT::unpack(cd[k], xd);
-#pragma unroll
-        for (int e = 0; e < VT::kElems; ++e)
-          acc += (double)draw_weight(xt[e], xd[e], 1, c, dp.mct, dp.izt, dp.mcd, dp.izd);
-      }
-      acc = sdv::wave_sum_d(acc);
-      if (lane == 0) bs[b] = acc;
-#pragma unroll
-      for (int k = 0; k < VL; ++k) {
-        ct[k] = nt[k];
-        cd[k] = nd[k];
-      }
+      __syncthreads();  // block sums of every wave visible to the workgroup
     }
-    __syncthreads();  // block sums of every wave visible to the workgroup
 
     // thread t owns the contiguous run of blocks [t*per, (t+1)*per)
     const int per = (n_blk + kFinThreads - 1) / kFinThreads;
@@ -628,17 +646,31 @@ __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec 
 // The finishing kernel, one workgroup per request: decide and draw at once
 // (every row read in one pass), or in rounds: decide only, recording the
 // draws, in every round but the last; the last decides the requests still
-// listed and makes every draw at once.
-enum { kFused = 0, kDecide = 1, kFinal = 2 };
+// listed and makes every draw at once.  For small batches the draws are
+// spread over the chip instead: the deciding phases record every draw
+// (kDecide over all requests, kFinalRec), k_draw_sums takes the residuals'
+// block sums with many workgroups per request, and kPick makes the draws.
+enum { kFused = 0, kDecide = 1, kFinal = 2, kFinalRec = 3, kPick = 4 };
 
 template <bool BF16, int PHASE>
 __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
   DrawRec rec;
   int r;
-  if constexpr (PHASE == kFinal) {
+  if constexpr (PHASE == kPick) {
     r = (int)blockIdx.x;
     rec = a.recs[r];
-    if (rec.kind == 3) finish_decide<BF16>(a, r, &rec);  // listed for this round
+    if (rec.kind == 1 || rec.kind == 2) finish_draw<BF16, true>(a, r, rec);
+    return;
+  } else if constexpr (PHASE == kFinal || PHASE == kFinalRec) {
+    r = (int)blockIdx.x;
+    rec = a.recs[r];
+    if (rec.kind == 3) {  // listed for this round
+      finish_decide<BF16>(a, r, &rec);
+      if constexpr (PHASE == kFinalRec) {
+        if (threadIdx.x == 0) a.recs[r] = rec;
+      }
+    }
+    if constexpr (PHASE == kFinalRec) return;
   } else {
     if (a.list && (int)blockIdx.x >= *a.count) return;
     r = a.list ? a.list[blockIdx.x] : (int)blockIdx.x;
@@ -648,7 +680,54 @@ __global__ __launch_bounds__(kFinThreads) void k_finish(VerifyArgs a) {
       return;
     }
   }
-  if (rec.kind == 1 || rec.kind == 2) finish_draw<BF16>(a, r, rec);
+  if (rec.kind == 1 || rec.kind == 2) finish_draw<BF16, false>(a, r, rec);
+}
+
+// Block sums of the residual draws recorded in a.recs: workgroup
+// (r, part) sums blocks [8 part, 8 part + 8) of request r's rejected row pair
+// into a.bsum, two blocks per wave, both loaded before either is summed.
+constexpr int kSumThreads = 256;
+constexpr int kSumWaves = kSumThreads / 64;
+constexpr int kSumBlocks = 2 * kSumWaves;  // residual blocks per workgroup
+
+template <bool BF16>
+__global__ __launch_bounds__(kSumThreads) void k_draw_sums(VerifyArgs a, int parts) {
+  using VT = sdv::Vec<BF16>;
+  constexpr int VL = kBlk / VT::kElems / 64;
+  constexpr int kBlkVec = kBlk / VT::kElems;
+  const int r = (int)(blockIdx.x / (unsigned)parts), part = (int)(blockIdx.x % (unsigned)parts);
+  const DrawRec rec = a.recs[r];
+  if (rec.kind != 1) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pos = rec.pos;
+  const uint4* tp = (const uint4*)(a.tgt + ((int64_t)a.tgt_row0[r] + (pos - 1)) * a.ld_bytes);
+  const uint4* dq = (const uint4*)(a.drf + ((int64_t)a.drf_row0[r] + (pos - 1)) * a.ld_bytes);
+  DrawParams dp;
+  dp.kind = 1;
+  dp.c = a.c;
+  dp.mct = rec.mct;
+  dp.izt = rec.izt;
+  dp.mcd = rec.mcd;
+  dp.izd = rec.izd;
+  const uint4 ninf = make_uint4(VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord, VT::kNegInfWord);
+  const int nvec = a.V / VT::kElems;
+  uint4 t[2][VL], d[2][VL];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = part * kSumBlocks + wave + i * kSumWaves;
+#pragma unroll
+    for (int k = 0; k < VL; ++k) {
+      const int v = b * kBlkVec + k * 64 + lane;  // v < nvec implies b < n_blk
+      t[i][k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
+      d[i][k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = part * kSumBlocks + wave + i * kSumWaves;
+    const double acc = sdv::wave_sum_d(block_lane_mass<BF16, VL>(t[i], d[i], dp));
+    if (lane == 0 && b < a.n_blk) a.bsum[(size_t)r * a.n_blk + b] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -739,9 +818,27 @@ size_t verify_ws_bytes(int R, int gmax, int V) {
 // for the requests that accepted every position so far.
 int next_cover(int cover) { return 2 * cover + 2; }
 
+// Draws spread over the chip: at most this many requests (measured: the two
+// extra launches cost more than they save once the requests fill the CUs).
+#ifndef SDV_WIDE_DRAW_MAX_R
+#define SDV_WIDE_DRAW_MAX_R 128
+#endif
+constexpr int kWideDrawMaxR = SDV_WIDE_DRAW_MAX_R;
+
+// The finishing launches of the last round: PHASE is kFused (one round) or
+// kFinal.
 template <bool BF16, int PHASE>
 int launch_finish(hipStream_t stream, int R, const VerifyArgs& a) {
-  SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16, PHASE>, dim3(R), dim3(kFinThreads), 0, stream, a));
+  if (R <= kWideDrawMaxR && (PHASE == kFused || PHASE == kFinal)) {
+    constexpr int kRec = PHASE == kFused ? kDecide : kFinalRec;
+    SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16, kRec>, dim3(R), dim3(kFinThreads), 0, stream, a));
+    const int parts = (a.n_blk + kSumBlocks - 1) / kSumBlocks;
+    SDV_TRY_LAUNCH(sdv::launch(k_draw_sums<BF16>, dim3((unsigned)((long long)R * parts)),
+                               dim3(kSumThreads), 0, stream, a, parts));
+    SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16, kPick>, dim3(R), dim3(kFinThreads), 0, stream, a));
+  } else {
+    SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16, PHASE>, dim3(R), dim3(kFinThreads), 0, stream, a));
+  }
   if (a.accept_prob && a.gmax > 0) {
     SDV_TRY_LAUNCH(sdv::launch(k_alpha_sums<BF16>, dim3((unsigned)((long long)R * a.gmax * a.n_ch)),
                                dim3(sdv::kRowThreads), 0, stream, a));

@@ -111,6 +111,21 @@ def test_verify_vocab_past_the_lds_block_sums():
         _full_check(inp, np.full(R, g))
 
 
+def test_verify_draws_in_the_request_workgroup():
+    """Batches of more than 128 requests make each correction draw inside the
+    request's own finishing workgroup (smaller batches spread the residual
+    sums over the chip): fp32 rows in one pass and in rounds, and bf16 rows
+    past the LDS block sums (V > 2M) on sampled requests."""
+    inp = _to_cuda(verify_inputs(R=130, gmax=3, V=5000, dtype=torch.float32, sigma_t=2.0,
+                                 sigma_d=(0.5, 3.0), seed=91))
+    _full_check(inp, np.full(130, 3))
+    _lazy_check(inp, np.full(130, 3))
+    inp = verify_inputs(R=130, gmax=1, V=2_100_000, dtype=torch.bfloat16, sigma_t=2.0, zipf=True,
+                        sigma_d=(1.0, 3.0), seed=92, device="cuda")
+    gpu, _ = _full_check(inp, np.full(130, 1), reqs=[0, 1, 64, 129])
+    assert np.all(to_np(gpu["status"]) == 0)
+
+
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
