@@ -126,6 +126,28 @@ def test_verify_draws_in_the_request_workgroup():
     assert np.all(to_np(gpu["status"]) == 0)
 
 
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 151936), (torch.float32, 5000)])
+def test_verify_draws_identical_in_either_path(dtype, V):
+    """The first 128 requests of a 129-request batch verified alone (draws
+    spread over the chip) and inside the batch (each draw in its request's
+    workgroup): identical outputs, bit for bit, in one pass and in rounds."""
+    R, g = 129, 6
+    inp = verify_inputs(R=R, gmax=g, V=V, dtype=dtype, sigma_t=3.0, zipf=True, sigma_d=(0.5, 3.0),
+                        seed=93, device="cuda")
+    ell = torch.full((R,), g, dtype=torch.int32, device="cuda")
+    for lazy in (False, True):
+        outs = []
+        for n in (R, R - 1):
+            o = sdv.sd_verify(inp["tgt"], inp["tgt_row0"][:n], inp["drf"], inp["drf_row0"][:n],
+                              inp["draft_tokens"][:n].contiguous(), ell[:n], V, 1.0, inp["seed"],
+                              probe=True, stats=True, stop_at_rejection=lazy)
+            torch.cuda.synchronize()
+            outs.append({k: to_np(v)[:R - 1] for k, v in o.items() if v is not None})
+        for k in outs[0]:
+            assert np.array_equal(outs[0][k], outs[1][k], equal_nan=True), (lazy, k)
+        assert np.all(outs[0]["status"] == 0)
+
+
 def test_verify_temperature_and_positions():
     inp = _to_cuda(verify_inputs(R=9, gmax=6, V=20000, dtype=torch.bfloat16, sigma_t=2.5,
                                  zipf=True, sigma_d=(0.5, 2.5), seed=78, temperature=0.7))
