@@ -8,13 +8,14 @@ every verify and draft row once).
 One step = sd_schedule (global argmax over the step's confidences; with this
 throughput table it keeps the full block, B = R * (1 + gamma) = 3072 rows)
 followed by sd_verify on the rows the schedule chose (ell read on the device,
-no host round trip).  Inputs are resident in HBM before timing starts; two
-input sets of 1.79 GB alternate between steps so the 256 MB last-level cache
+no host round trip).  Inputs are resident in HBM before timing starts; three
+input sets of 1.79 GB rotate between steps so the 256 MB last-level cache
 cannot serve repeats.
 
 Also reported: the oracle timed on the host's cores on a bounded sample of
-the same step (cpu_baseline), and the Markov drafting head at R=128,
-gamma=16, V=129280, rank 256 (markov_draft).
+the same step (cpu_baseline); the ragged asynchronous step (R=512,
+gamma_r in 1..16), the mid-size and the tiny step; the Markov and RNN drafting
+heads at R=128, gamma=16, V=129280.
 """
 
 import argparse
@@ -64,6 +65,32 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+class ReadProbe:
+    """The plain streaming read of libsdv_probe.so (built beside libsdv by
+    __graft_entry__.build()): the practical HBM read ceiling."""
+
+    def __init__(self):
+        path = os.path.join(ROOT, "draft_verification_amd", "libsdv_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        self.lib = ctypes.CDLL(path)
+        self.lib.probe_stream_read_sink_words.restype = ctypes.c_longlong
+        self.lib.probe_stream_read_sink_words.argtypes = [ctypes.c_longlong]
+        self.lib.probe_stream_read.restype = ctypes.c_int
+        self.lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
+                                               ctypes.c_void_p]
+
+    def sink_words(self, nbytes):
+        return int(self.lib.probe_stream_read_sink_words(nbytes))
+
+    def read(self, torch, src, sink):
+        nbytes = src.numel() * src.element_size()
+        rc = self.lib.probe_stream_read(torch.cuda.current_stream().cuda_stream, src.data_ptr(), nbytes,
+                                        sink.data_ptr())
+        if rc != 0:
+            raise RuntimeError(f"probe_stream_read failed: {rc}")
 
 
 def source_hash():
@@ -164,6 +191,134 @@ def bench_early_stop(sdv, torch, sets, bufs, ws, sws, steps):
     return {"verify_rows": blocks, "us_per_step": round(ms * 1e3, 1),
             "rows_per_s": round(B / (ms / 1e3), 1),
             "note": "the chosen rows of all input sets fit in the 256 MB last-level cache"}
+
+
+def pct(xs):
+    """Median, 10th and 90th percentile of a list of per-step times (us)."""
+    import numpy as np
+    return {"median": round(float(np.percentile(xs, 50)), 1), "p10": round(float(np.percentile(xs, 10)), 1),
+            "p90": round(float(np.percentile(xs, 90)), 1)}
+
+
+def timed_steps(torch, step, n_sets, warmup, steps, prof=None):
+    """Run `warmup` untimed then `steps` timed calls of step(i, prof_pair),
+    rotating over n_sets input sets; per-step times from events between the
+    steps (on the current stream, where the library's kernels run), and, when
+    prof holds 2 * steps raw HIP events, the bandwidth pass's time per step."""
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        step(i, (prof[2 * i], prof[2 * i + 1]) if prof else None)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+
+
+def bench_config(sdv, torch, hip, name, n_sets, steps, warmup, graph_steps=False):
+    """One of the other schedule + verify workloads: tiny (R=4, gamma=4,
+    V=1024 fp32), mid (R=64, gamma=8, V=32000 bf16) or ragged (R=512,
+    gamma_r in 1..16, V=151936 bf16; the asynchronous capacity chain: global
+    argmax on the previous step's confidences, then the top K of the current
+    ones).  n_sets input sets rotate; graph_steps times steps replayed from
+    a captured graph (steps shorter than the host's per-call overhead)."""
+    import numpy as np
+    from workloads import verify_config
+    dev = "cuda"
+    sets = [verify_config(name, device=dev, data_shift=i) for i in range(n_sets)]
+    R, g, V = sets[0]["R"], sets[0]["gmax"], sets[0]["V"]
+    esize = sets[0]["tgt"].element_size()
+    ragged = name == "ragged"
+
+    def outs():
+        return (dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+                     batch=torch.empty(1, dtype=torch.int32, device=dev),
+                     n_sel=torch.empty(1, dtype=torch.int32, device=dev),
+                     theta=torch.empty(1, dtype=torch.float64, device=dev),
+                     surv=torch.empty((R, g), dtype=torch.float32, device=dev)),
+                dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+                     batch=torch.empty(1, dtype=torch.int32, device=dev),
+                     n_sel=torch.empty(1, dtype=torch.int32, device=dev),
+                     theta=torch.empty(1, dtype=torch.float64, device=dev),
+                     surv=torch.empty((R, g), dtype=torch.float32, device=dev)),
+                dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                     tokens=torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+                     status=torch.empty(R, dtype=torch.int32, device=dev)))
+    bufs = [outs() for _ in sets]
+    ws = torch.empty(sdv.sd_verify_workspace_size(R, g, V), dtype=torch.uint8, device=dev)
+    sws = torch.empty(sdv.sd_schedule_workspace_size(R, g), dtype=torch.uint8, device=dev)
+
+    def step(i, prof=None):
+        inp = sets[i % n_sets]
+        po, so, vo = bufs[i % n_sets]
+        if ragged:
+            first = sdv.sd_schedule(inp["conf_prev"], inp["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX,
+                                    gamma_r=inp["gamma_r"], out=po, workspace=sws)
+            sch = sdv.sd_schedule(inp["conf"], inp["sps"], sdv.SD_SCHED_CAPPED_TOPK, gamma_r=inp["gamma_r"],
+                                  cap_k=first["n_sel"], out=so, workspace=sws)
+        else:
+            sch = sdv.sd_schedule(inp["conf"], inp["sps"], sdv.SD_SCHED_GLOBAL_ARGMAX, out=so,
+                                  workspace=sws)
+        sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
+                      sch["ell"], V, inp["temperature"], inp["seed"], workspace=ws, out=vo,
+                      prof_events=prof)
+
+    for i in range(n_sets):
+        step(i)
+    torch.cuda.synchronize()
+    ells = [bufs[i][1]["ell"].cpu().numpy().astype(np.int64) for i in range(n_sets)]
+    rows = [int(np.sum(1 + e)) for e in ells]                       # B per set
+    alg = [esize * V * (int(np.sum(1 + e)) + int(np.sum(e))) for e in ells]   # every batch row once
+    res = {"workload": "", "R": R, "gamma_max": g, "V": V, "dtype": "bf16" if esize == 2 else "f32",
+           "input_sets": n_sets, "input_bytes_total": int(sum(alg)),
+           "verify_rows_per_set": rows}
+    if graph_steps:
+        # one replay = one step of every input set in turn
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(n_sets):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(max(warmup, 2)):
+            graph.replay()
+        torch.cuda.synchronize()
+        n_rep = max(10, steps // n_sets)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+        ev[0].record()
+        for k in range(n_rep):
+            graph.replay()
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[k].elapsed_time(ev[k + 1]) * 1e3 / n_sets for k in range(n_rep)]
+        res["timing"] = (f"{n_rep} replays of a captured graph holding one step of each of the "
+                         f"{n_sets} input sets; percentiles over replays of the per-step mean")
+        res["us_per_step"] = pct(per)
+        mean_us = float(np.mean(per))
+        res["rows_per_s"] = round(float(np.mean(rows)) / (mean_us / 1e6), 1)
+        res["all_rows_GBps"] = round(float(np.mean(alg)) / (mean_us / 1e6) / 1e9, 1)
+        return res
+    kev = hip.create(2 * steps)
+    per = timed_steps(torch, step, n_sets, warmup, steps, prof=kev)
+    k_us = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) * 1e3 for i in range(steps)]
+    hip.destroy(kev)
+    step_rows = [rows[i % n_sets] for i in range(steps)]
+    step_bytes = [alg[i % n_sets] for i in range(steps)]
+    achieved = sum(step_bytes) / (sum(k_us) / 1e6) / 1e9
+    res["timing"] = f"{steps} steps after {warmup} warm-up, events between steps"
+    res["us_per_step"] = pct(per)
+    res["rows_per_s"] = round(sum(step_rows) / (sum(per) / 1e6), 1)
+    res["bandwidth_pass"] = {"achieved_GBps": round(achieved, 1), "peak_GBps": HBM_PEAK_GBS,
+                             "frac": round(achieved / HBM_PEAK_GBS, 4), "us": pct(k_us),
+                             "bytes_per_launch_mean": int(np.mean(step_bytes)),
+                             "what": "k_row_partials: every verify and draft row of the batch read "
+                                     "once, 2 bytes x V per row"}
+    res["all_rows_GBps"] = round(sum(step_bytes) / (sum(per) / 1e6) / 1e9, 1)
+    return res
 
 
 def graph_time_us(torch, fn, calls=10, replays=10):
@@ -374,6 +529,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-markov", action="store_true")
     ap.add_argument("--no-early-stop", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the ragged asynchronous, mid-size and tiny steps")
     ap.add_argument("--sweep", action="store_true",
                     help="only time verification alone at R = 16, 64, 256, 1024 (headline distributions, "
                          "full blocks), in one pass and in rounds, then exit")
@@ -446,15 +603,15 @@ def main():
     K = args.steps
     kev = hip.create(2 * K)
     print(f"timing {K} steps", file=sys.stderr, flush=True)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
-    t0.record()
+    sev[0].record()
     for i in range(K):
         step(i, prof=(kev[2 * i], kev[2 * i + 1]))
-    t1.record()
+        sev[i + 1].record()
     torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
+    ms_total = sev[0].elapsed_time(sev[K])
+    step_us = [sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(K)]
     k_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(K)]
     hip.destroy(kev)
     ms_per_step = ms_total / K
@@ -553,18 +710,18 @@ def main():
     # practical read ceiling: a plain streaming read of a buffer of the batch's
     # size with the bandwidth pass's load shape (two buffers alternate)
     bytes_launch = headline_bytes(R, g, V)
+    probe = ReadProbe()
     rbufs = [torch.empty(bytes_launch, dtype=torch.uint8, device=dev)
              for _ in range(2)]
-    sink = torch.empty(max(sdv.lib().sd_stream_read_sink_words(bytes_launch), 1), dtype=torch.int32,
-                       device=dev)
+    sink = torch.empty(max(probe.sink_words(bytes_launch), 1), dtype=torch.int32, device=dev)
     for i in range(4):
-        sdv.sd_stream_read(rbufs[i % 2], sink=sink)
+        probe.read(torch, rbufs[i % 2], sink)
     torch.cuda.synchronize()
     r0 = torch.cuda.Event(enable_timing=True)
     r1 = torch.cuda.Event(enable_timing=True)
     r0.record()
     for i in range(20):
-        sdv.sd_stream_read(rbufs[i % 2], sink=sink)
+        probe.read(torch, rbufs[i % 2], sink)
     r1.record()
     torch.cuda.synchronize()
     read_us = r0.elapsed_time(r1) / 20 * 1e3
@@ -600,6 +757,7 @@ def main():
                    "R": R, "gamma": g, "V": V, "verify_rows": rows, "draft_rows": R * g,
                    "input_sets": len(sets)},
         "roofline": roofline,
+        "step_us": pct(step_us),
         "breakdown_us": {"step": round(ms_per_step * 1e3, 1), "schedule": round(sched_us, 1),
                          "verify": round(verify_us, 1), "row_stats_kernel": round(k_avg * 1e3, 1)},
         "verify_only": {"rows_per_s": round(rows / (verify_us / 1e6), 1),
@@ -631,6 +789,29 @@ def main():
     if not args.no_early_stop:
         print("early-stop schedule", file=sys.stderr, flush=True)
         result["early_stop_block"] = bench_early_stop(sdv, torch, sets, bufs, ws, sws, K)
+    if not args.no_configs:
+        # the other workloads, after the headline's inputs are released (the
+        # first set stays for the oracle's timing at the end)
+        sets = sets[:1]
+        del bufs, dstats, ref_tokens, ells
+        torch.cuda.empty_cache()
+        print("ragged asynchronous step", file=sys.stderr, flush=True)
+        rg = bench_config(sdv, torch, hip, "ragged", 3, K, args.warmup)
+        rg["workload"] = ("ragged async step: R=512 requests, gamma_r ~ U{1..16}, V=151936 bf16; "
+                          "global argmax on the previous confidences caps the batch, the top K of "
+                          "the current ones fill it, then verification")
+        result["ragged_async"] = rg
+        torch.cuda.empty_cache()
+        print("mid-size step", file=sys.stderr, flush=True)
+        md = bench_config(sdv, torch, hip, "mid", 8, K, args.warmup)
+        md["workload"] = "mid step: R=64, gamma=8, V=32000 bf16, global argmax schedule + verification"
+        mdg = bench_config(sdv, torch, hip, "mid", 8, K, args.warmup, graph_steps=True)
+        md["graph_replay"] = {k: mdg[k] for k in ("timing", "us_per_step", "rows_per_s", "all_rows_GBps")}
+        result["mid"] = md
+        print("tiny step", file=sys.stderr, flush=True)
+        tn = bench_config(sdv, torch, hip, "tiny", 1, K, args.warmup, graph_steps=True)
+        tn["workload"] = "tiny step: R=4, gamma=4, V=1024 fp32, global argmax schedule + verification"
+        result["tiny"] = tn
     if not args.no_markov:
         print("markov head", file=sys.stderr, flush=True)
         result["markov_draft"] = bench_markov(sdv, torch, K, hip)

@@ -18,7 +18,7 @@ from ._lib import (  # noqa: F401
     sd_markov_draft_workspace_size,
     sd_rnn_draft,
     sd_rnn_draft_workspace_size,
-    sd_stream_read,
+    sd_uniforms,
     sd_lightspec_update,
     sd_lightspec_plan,
     SD_SCHED_EARLY_STOP,

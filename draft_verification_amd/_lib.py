@@ -7,6 +7,8 @@ fallback.
 """
 
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
@@ -42,7 +44,7 @@ EXPORTS = (
     "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
     "sd_rnn_draft_workspace_size", "sd_rnn_draft",
     "sd_lightspec_update", "sd_lightspec_plan_workspace_size", "sd_lightspec_plan",
-    "sd_stream_read_sink_words", "sd_stream_read",
+    "sd_uniforms",
 )
 
 
@@ -97,10 +99,8 @@ def lib():
     L.sd_lightspec_plan.restype = _I
     L.sd_lightspec_plan.argtypes = [_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _SZ]
-    L.sd_stream_read_sink_words.restype = ctypes.c_longlong
-    L.sd_stream_read_sink_words.argtypes = [ctypes.c_longlong]
-    L.sd_stream_read.restype = _I
-    L.sd_stream_read.argtypes = [_P, _P, ctypes.c_longlong, _P]
+    L.sd_uniforms.restype = _I
+    L.sd_uniforms.argtypes = [_P, _U64, ctypes.c_longlong, _P, _P, _I, _P]
     _lib = L
     return L
 
@@ -135,6 +135,24 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _on_stream(fn):
+    """Run fn with its `stream` argument as torch's current stream, so the
+    outputs and the temporary workspace it allocates belong to the stream the
+    kernels are enqueued on: when the workspace is freed on return, the
+    caching allocator hands that block only to later work of the same stream,
+    never to another stream while these kernels may still use it.  Outputs
+    and workspaces the caller passes in are the caller's to keep alive on
+    that stream."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        stream = sig.bind_partial(*args, **kw).arguments.get("stream")
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return wrapper
+
+
 def _check(fn, code):
     if code != SD_OK:
         raise SdvError(fn, code)
@@ -149,6 +167,7 @@ def sd_schedule_workspace_size(R, gmax):
     return lib().sd_schedule_workspace_size(R, gmax)
 
 
+@_on_stream
 def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, workspace=None,
                 stream=None, sts_temp=None, threshold=0.0):
     """Run the scheduler.  conf [R][gmax] fp32, sps fp32, gamma_r [R] int32 or
@@ -180,6 +199,7 @@ def sd_verify_workspace_size(R, gmax, V):
     return lib().sd_verify_workspace_size(R, gmax, V)
 
 
+@_on_stream
 def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.0, seed=0,
               pos0=None, probe=False, stats=False, alpha=False, workspace=None, out=None,
               stream=None, prof_events=None, drf_stats=None, stop_at_rejection=False):
@@ -232,6 +252,7 @@ def sd_markov_draft_workspace_size(R, gamma, V, rank):
     return lib().sd_markov_draft_workspace_size(R, gamma, V, rank)
 
 
+@_on_stream
 def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, workspace=None,
                     out=None, stream=None, stats=False):
     """Run the Markov drafting head.  Returns a dict of device tensors:
@@ -266,6 +287,7 @@ def sd_rnn_draft_workspace_size(R, gamma, V, d):
     return lib().sd_rnn_draft_workspace_size(R, gamma, V, d)
 
 
+@_on_stream
 def sd_rnn_draft(U, W, Es, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, workspace=None,
                  out=None, stream=None, stats=False):
     """Run the RNN drafting head.  Returns a dict of device tensors:
@@ -296,21 +318,22 @@ def sd_rnn_draft(U, W, Es, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, 
     return dict(tokens=tokens, q_logits=ql, conf=conf, status=status, q_stats=qs)
 
 
-def sd_stream_read(src, sink=None, stream=None):
-    """Measurement aid: stream every byte of the contiguous GPU tensor `src`
-    with the bandwidth pass's load shape (see sd_stream_read in sdv.h).
-    Returns the sink tensor (one uint32 fold per workgroup, as int32)."""
-    nbytes = src.numel() * src.element_size()
-    words = lib().sd_stream_read_sink_words(nbytes)
-    if sink is None:
-        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
-    elif sink.numel() < words:
-        raise ValueError(f"sink needs {words} words")
-    _check("sd_stream_read", lib().sd_stream_read(_stream(stream), _ptr(src, name="src"), nbytes,
-                                                  _ptr(sink, torch.int32, "sink")))
-    return sink
+@_on_stream
+def sd_uniforms(seed, req, pos, draw, out=None, stream=None):
+    """The uniforms u(seed, req[i], pos[i], draw) the library's decisions
+    draw (req, pos int64 device tensors of one length).  Returns fp32."""
+    n = req.numel()
+    if pos.numel() != n:
+        raise ValueError("req and pos must have the same length")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=req.device)
+    _check("sd_uniforms", lib().sd_uniforms(_stream(stream), int(seed) & (2**64 - 1), n,
+                                            _ptr(req, torch.int64, "req"), _ptr(pos, torch.int64, "pos"),
+                                            int(draw), _ptr(out, torch.float32, "out")))
+    return out
 
 
+@_on_stream
 def sd_lightspec_update(alpha, ell, status, lam, ema, count, stream=None):
     """Fold one verify step's acceptance probabilities alpha [R][gmax] fp32
     into the per-position EMA state ema [gmax] fp64 / count [gmax] int64
@@ -322,6 +345,7 @@ def sd_lightspec_update(alpha, ell, status, lam, ema, count, stream=None):
         _ptr(count, torch.int64, "count")))
 
 
+@_on_stream
 def sd_lightspec_plan(ema, count, d_prev, sps, draft_cost, out=None, workspace=None, stream=None):
     """Both planning stages.  d_prev [R] int32 (the previous round's draft
     lengths).  Returns a dict of device tensors: conf (planning confidences),

@@ -1,4 +1,6 @@
-"""Compile libsdv.so (HIP for gfx950) in-tree with hipcc."""
+"""Compile libsdv.so (HIP for gfx950) in-tree with hipcc, and beside it
+libsdv_probe.so, the benchmark's plain streaming read (a measurement aid that
+is not part of the library's interface)."""
 
 import os
 import shutil
@@ -9,7 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsdv.so")
 SOURCES = ["abi.hip", "schedule.hip", "row_partials.hip", "verify.hip", "markov.hip", "lightspec.hip",
-           "probe.hip"]
+           "uniforms.hip"]
+PROBE_LIB = os.path.join(PKG, "libsdv_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -32,10 +36,9 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    """Build libsdv.so next to this file and return its path (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + srcs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -44,7 +47,14 @@ def build(verbose: bool = False) -> str:
         err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
         if err.strip():
             print(err)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libsdv.so and libsdv_probe.so next to this file and return the
+    library's path (always recompiles)."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

@@ -472,7 +472,11 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       }
     }
     __syncthreads();
-    if (s_tile < 0) {  // rounding pushed the target past the end: last tile with mass
+    // every thread reads the claim's result before thread 0 may rewrite it
+    // below, so the branch (and its barriers) is taken by all or by none
+    const bool missed = s_tile < 0;
+    if (missed) {  // rounding pushed the target past the end: last tile with mass
+      __syncthreads();
       if (tid == 0) {
         for (int t = n_tiles - 1; t >= 0; --t)
           if (pp[t].y > 0.0f) {

@@ -1,8 +1,15 @@
-// Measurement aid, not part of the method: a plain streaming read with the
-// same load shape as the bandwidth pass of sd_verify (256-thread workgroups,
-// eight 16-byte non-temporal loads per thread, 32 KB per workgroup).  Its
-// duration over a buffer of the batch's size is the practical HBM read
-// ceiling that the bandwidth pass is compared with.
+// libsdv_probe: the benchmark's measurement aid, built beside libsdv and not
+// part of its interface.  A plain streaming read with the same load shape as
+// the bandwidth pass of sd_verify (256-thread workgroups, eight 16-byte
+// non-temporal loads per thread, 32 KB per workgroup); its duration over a
+// buffer of the batch's size is the practical HBM read ceiling that the
+// bandwidth pass is compared with.
+//
+//   long long probe_stream_read_sink_words(long long bytes)
+//       uint32 words the sink needs for `bytes` (-1 for bytes < 0)
+//   int probe_stream_read(hipStream_t s, const void* src, long long bytes, uint32_t* sink)
+//       stream `bytes` (a multiple of 16) of 16-byte aligned device memory,
+//       folding each workgroup's words into one sink word; SD_* return codes
 #include "sdv_common.h"
 #include "sdv_host.h"
 
@@ -31,12 +38,12 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* __restric
 
 }  // namespace
 
-extern "C" long long sd_stream_read_sink_words(long long bytes) {
+extern "C" long long probe_stream_read_sink_words(long long bytes) {
   if (bytes < 0) return -1;
   return (bytes / 16 + kVecPerBlock - 1) / kVecPerBlock;
 }
 
-extern "C" int sd_stream_read(hipStream_t stream, const void* src, long long bytes, uint32_t* sink) {
+extern "C" int probe_stream_read(hipStream_t stream, const void* src, long long bytes, uint32_t* sink) {
   if (bytes < 0 || (bytes % 16) != 0) return SD_EINVAL;
   if (bytes == 0) return SD_OK;
   if (!src || !sink || (((uintptr_t)src) & 15) != 0) return SD_EINVAL;

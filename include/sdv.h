@@ -9,6 +9,10 @@
  *   sd_verify        lossless rejection sampling over full vocabulary rows
  *   sd_markov_draft  the low-rank Markov drafting head and the confidence head
  *
+ * and around them: sd_rnn_draft (the RNN form of the drafting head), the
+ * budget planner (sd_lightspec_update, sd_lightspec_plan) and sd_uniforms
+ * (the uniforms behind the random decisions).
+ *
  * Sources, by page and section:
  *   [DS]  "DSpark: Confidence-Scheduled Speculative Decoding with
  *         Semi-Autoregressive Generation" (paper summary page):
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 3
+#define SDV_ABI_VERSION 4
 
 /* return codes (host side) */
 #define SD_OK             0
@@ -114,7 +118,8 @@ const char* sd_status_string(int code);
  *   Theta_n = tau_n * sps[R + n - 1]   (fp64; Theta_0 = 0)
  * where sps[B-1] is the verification throughput at batch B = R + n.
  *   mode EARLY_STOP:    n* = (first n >= 1 with Theta_n < Theta_{n-1}) - 1,
- *                       else N  [DS 2.2 "stop once throughput falls"]
+ *                       else N  [DS 2.2: the greedy stop at the first
+ *                       drop of the throughput estimate]
  *   mode GLOBAL_ARGMAX: n* = smallest n maximising Theta_n over n = 0..N
  *   mode CAPPED_TOPK:   n* = min(max(*cap_k, 0), N): the capacity was fixed
  *                       before these confidences were known [DS challenge 2];
@@ -362,19 +367,20 @@ int sd_lightspec_plan(hipStream_t stream, int R, int gamma_max, const double* em
                       void* workspace, size_t workspace_bytes);
 
 /*
- * Measurement aid, not part of the method.
- *
- * sd_stream_read - stream `bytes` bytes of device memory at `src` with the
- * load shape of sd_verify's bandwidth pass (256-thread workgroups, eight
- * 16-byte non-temporal loads per thread, 32 KB per workgroup) and fold each
- * workgroup's words into one uint32 of `sink`.  Timing it over a buffer of
- * the verify batch's size gives the practical HBM read ceiling.
- *   bytes >= 0, bytes % 16 == 0; src 16-byte aligned device memory;
- *   sink: device memory for sd_stream_read_sink_words(bytes) uint32.
- * Returns SD_EINVAL on a bad size or pointer, SD_ELAUNCH if the launch fails.
+ * sd_uniforms - the uniforms the library's random decisions draw, for callers
+ * that replay or audit a step [SD 1.1: the accept test and the correction
+ * sample; DS innovation one: the draft sample]:
+ *     out[i] = u(seed, req[i], pos[i], draw)
+ * with the counter hash given at the top of this header (req and pos taken
+ * as unsigned 64-bit words, so pos[i] = pos0[r] + position reproduces the
+ * counter a call with that pos0 used).  The 24-bit values are exact in fp32.
+ *   n >= 0; req, pos [n] int64 and out [n] fp32, device memory; draw >= 0
+ *   (0 draft sample, 1 accept test, 2 correction sample).
+ * Returns SD_EINVAL on a bad size, draw or null pointer (n > 0),
+ * SD_EUNSUPPORTED past 2^31 - 1 workgroups, SD_ELAUNCH if the launch fails.
  */
-long long sd_stream_read_sink_words(long long bytes);
-int sd_stream_read(hipStream_t stream, const void* src, long long bytes, uint32_t* sink);
+int sd_uniforms(hipStream_t stream, uint64_t seed, long long n, const int64_t* req,
+                const int64_t* pos, int draw, float* out);
 
 #ifdef __cplusplus
 }

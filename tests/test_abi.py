@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sdv.sd_abi_version() == 3
+    assert sdv.sd_abi_version() == 4
     assert sdv.sd_status_string(0) == "ok"
     for code in (-1, -2, -3, -4, 1, 2, 4, 8, 16):
         assert sdv.sd_status_string(code) != "unknown status"
@@ -117,17 +117,33 @@ def test_markov_host_validation():
     assert _mk(qstats=260) == _lib.SD_EINVAL                        # (m, Z) pairs need 8 bytes
 
 
-def test_stream_read_host_validation():
+def test_uniforms_host_validation():
     L = sdv.lib()
-    assert L.sd_stream_read_sink_words(0) == 0
-    assert L.sd_stream_read_sink_words(32768) == 1
-    assert L.sd_stream_read_sink_words(32784) == 2
-    assert L.sd_stream_read_sink_words(-16) == -1
     p = ctypes.c_void_p(256)
-    assert L.sd_stream_read(None, p, 24, p) == _lib.SD_EINVAL        # not a multiple of 16
-    assert L.sd_stream_read(None, None, 32, p) == _lib.SD_EINVAL     # no source
-    assert L.sd_stream_read(None, ctypes.c_void_p(8), 32, p) == _lib.SD_EINVAL   # misaligned
-    assert L.sd_stream_read(None, p, 0, None) == _lib.SD_OK          # nothing to read
+    assert L.sd_uniforms(None, 1, -1, p, p, 0, p) == _lib.SD_EINVAL          # negative size
+    assert L.sd_uniforms(None, 1, 4, p, p, -1, p) == _lib.SD_EINVAL          # negative draw
+    assert L.sd_uniforms(None, 1, 4, None, p, 0, p) == _lib.SD_EINVAL        # no request ids
+    assert L.sd_uniforms(None, 1, 4, p, p, 0, None) == _lib.SD_EINVAL        # no output
+    assert L.sd_uniforms(None, 1, 0, None, None, 2, None) == _lib.SD_OK      # nothing to draw
+
+
+def test_read_probe_is_outside_the_library():
+    """The benchmark's streaming read lives in libsdv_probe.so, not in the
+    library's interface; its host checks."""
+    assert not hasattr(ctypes.CDLL(_lib._LIB_PATH), "probe_stream_read")
+    P = ctypes.CDLL(os.path.join(os.path.dirname(_lib._LIB_PATH), "libsdv_probe.so"))
+    P.probe_stream_read_sink_words.restype = ctypes.c_longlong
+    P.probe_stream_read_sink_words.argtypes = [ctypes.c_longlong]
+    P.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    assert P.probe_stream_read_sink_words(0) == 0
+    assert P.probe_stream_read_sink_words(32768) == 1
+    assert P.probe_stream_read_sink_words(32784) == 2
+    assert P.probe_stream_read_sink_words(-16) == -1
+    p = ctypes.c_void_p(256)
+    assert P.probe_stream_read(None, p, 24, p) == _lib.SD_EINVAL        # not a multiple of 16
+    assert P.probe_stream_read(None, None, 32, p) == _lib.SD_EINVAL     # no source
+    assert P.probe_stream_read(None, ctypes.c_void_p(8), 32, p) == _lib.SD_EINVAL   # misaligned
+    assert P.probe_stream_read(None, p, 0, None) == _lib.SD_OK          # nothing to read
 
 
 def test_lightspec_host_validation():

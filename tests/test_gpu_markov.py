@@ -196,7 +196,9 @@ def test_markov_degenerate_anchor_and_rows():
     check_chain(inp, out, ref, [0])                           # no bias, no embedding: still exact
 
 
-SAMPLED = (0, 5, 77, 127)
+# sixteen requests spread over R = 128 whose logits and (m, Z) are compared
+# element by element at every position along the shared history
+SAMPLED = (0, 8, 17, 25, 34, 42, 51, 59, 68, 76, 85, 93, 102, 110, 119, 127)
 
 
 @pytest.fixture(scope="module")
@@ -210,8 +212,8 @@ def workload():
 
 
 def test_markov_draft_workload_sampled(workload):
-    """Logits and (m, Z) on sampled requests, confidences and tokens of every
-    request along the shared histories."""
+    """Logits and (m, Z) on sixteen requests spread over the batch,
+    confidences and tokens of every request along the shared histories."""
     inp, out, ref = workload
     assert np.all(to_np(out["status"]) == 0)
     compared, parted, _ = check_chain(inp, out, ref, range(inp["R"]))

@@ -172,12 +172,13 @@ def test_rnn_degenerate_anchor_and_rows():
 
 def test_rnn_draft_workload_sampled():
     """R=128, gamma=16, V=129280, d=128: the oracle's chain for every request;
-    logits and (m, Z) on sampled requests, confidences and tokens everywhere
-    along the shared histories."""
+    logits and (m, Z) on sixteen requests spread over the batch, confidences
+    and tokens everywhere along the shared histories."""
     inp = rnn_config(device="cuda")
     out = _run(inp)
     assert np.all(to_np(out["status"]) == 0)
-    ref = oracle_chain(inp, range(inp["R"]), keep=(0, 77, 127))
+    keep = (0, 8, 17, 25, 34, 42, 51, 59, 68, 76, 85, 93, 102, 110, 119, 127)   # spread over R = 128
+    ref = oracle_chain(inp, range(inp["R"]), keep=keep)
     compared, parted, _ = check_chain(inp, out, ref, range(inp["R"]))
     assert parted <= partings_bound(compared)
 
