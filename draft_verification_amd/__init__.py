@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     sd_schedule_workspace_size,
     sd_verify,
     sd_verify_workspace_size,
+    sd_verify_noalloc,
     sd_markov_draft,
     sd_markov_draft_workspace_size,
     sd_rnn_draft,

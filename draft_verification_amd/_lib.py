@@ -44,7 +44,7 @@ EXPORTS = (
     "sd_verify", "sd_markov_draft_workspace_size", "sd_markov_draft",
     "sd_rnn_draft_workspace_size", "sd_rnn_draft",
     "sd_lightspec_update", "sd_lightspec_plan_workspace_size", "sd_lightspec_plan",
-    "sd_uniforms",
+    "sd_uniforms", "sd_verify_noalloc",
 )
 
 
@@ -99,6 +99,9 @@ def lib():
     L.sd_lightspec_plan.restype = _I
     L.sd_lightspec_plan.argtypes = [_P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _SZ]
+    L.sd_verify_noalloc.restype = _I
+    L.sd_verify_noalloc.argtypes = [_P, _I, _I, _I, _I, _I, ctypes.c_float, _U64, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _I]
     L.sd_uniforms.restype = _I
     L.sd_uniforms.argtypes = [_P, _U64, ctypes.c_longlong, _P, _P, _I, _P]
     _lib = L
@@ -246,6 +249,37 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
         *(prof_events if prof_events else (None, None)))
     _check("sd_verify", code)
     return dict(n_acc=n_acc, tokens=toks, status=status, probe=pp, row_stats=rs, alpha=al)
+
+
+@_on_stream
+def sd_verify_noalloc(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.0, seed=0,
+                      pos0=None, drf_stats=None, stop_at_rejection=False, out=None, stream=None):
+    """sd_verify through the entry point that allocates nothing: the library
+    holds the workspace.  The caller passes every output in `out` (n_acc,
+    tokens, status, and optionally probe, row_stats, alpha), as a caller
+    that cannot allocate would; returns `out`."""
+    R, gmax = draft_tokens.shape
+    if tgt.dtype == torch.bfloat16:
+        dt = SD_DTYPE_BF16
+    elif tgt.dtype == torch.float32:
+        dt = SD_DTYPE_F32
+    else:
+        raise TypeError("logits must be bf16 or fp32")
+    if drf.dtype != tgt.dtype or drf.shape[1] != tgt.shape[1]:
+        raise ValueError("target and draft rows must share dtype and leading dimension")
+    o = out
+    code = lib().sd_verify_noalloc(
+        _stream(stream), R, gmax, int(V), tgt.shape[1], dt, float(temperature), int(seed) & (2**64 - 1),
+        _ptr(pos0, torch.int64, "pos0"), _ptr(tgt, None, "tgt"), _ptr(tgt_row0, torch.int32, "tgt_row0"),
+        _ptr(drf, None, "drf"), _ptr(drf_row0, torch.int32, "drf_row0"),
+        _ptr(drf_stats, torch.float32, "drf_stats"),
+        _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(ell, torch.int32, "ell"),
+        _ptr(o["n_acc"], torch.int32, "n_acc"), _ptr(o["tokens"], torch.int32, "tokens"),
+        _ptr(o["status"], torch.int32, "status"), _ptr(o.get("probe"), torch.float32, "probe"),
+        _ptr(o.get("row_stats"), torch.float32, "row_stats"), _ptr(o.get("alpha"), torch.float32, "alpha"),
+        SD_VERIFY_STOP_AT_REJECTION if stop_at_rejection else 0)
+    _check("sd_verify_noalloc", code)
+    return o
 
 
 def sd_markov_draft_workspace_size(R, gamma, V, rank):

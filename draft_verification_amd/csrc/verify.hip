@@ -41,6 +41,8 @@
 //                   1 - TV(p, q), the confidence label of the DSpark summary
 //                   ("2.1")
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "sdv_host.h"
 #include "verify_common.h"
@@ -1004,4 +1006,58 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
     prev = cover;
   }
   return SD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// sd_verify_noalloc: sd_verify with its workspace held by the library, for
+// callers that cannot allocate (code under graph capture, serving loops that
+// forbid allocation).  The workspace is one file-scope device array; each GPU
+// holds its own copy at its own address, looked up once per device with that
+// device current.  Every workspace word a call reads is first written by the
+// same call's kernels (the round counters are zeroed by a kernel of the round
+// before), so no call depends on what an earlier one left there; calls that
+// overlap on one GPU share the array and race.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = SD_VERIFY_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kNoAllocMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device (null on error).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int sd_verify_noalloc(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype,
+                                 float temperature, uint64_t seed, const int64_t* pos0,
+                                 const void* tgt_logits, const int32_t* tgt_row0, const void* drf_logits,
+                                 const int32_t* drf_row0, const float* drf_stats,
+                                 const int32_t* draft_tokens, const int32_t* ell, int32_t* n_accepted,
+                                 int32_t* out_tokens, int32_t* status, float* probe_probs,
+                                 float* row_stats, float* accept_prob, int options) {
+  if (R < 0 || gamma_max < 0 || V < 8) return SD_EINVAL;
+  if (gamma_max > SD_MAX_GAMMA || V > SD_MAX_VOCAB) return SD_EUNSUPPORTED;
+  if (R == 0) return SD_OK;
+  if (verify_ws_bytes(R, gamma_max, V) > kNoAllocScratchBytes) return SD_ERANGE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return SD_ELAUNCH;
+  return sd_verify(stream, R, gamma_max, V, ld, dtype, temperature, seed, pos0, tgt_logits, tgt_row0,
+                   drf_logits, drf_row0, drf_stats, draft_tokens, ell, n_accepted, out_tokens, status,
+                   probe_probs, row_stats, accept_prob, options, ws, kNoAllocScratchBytes, nullptr,
+                   nullptr);
 }

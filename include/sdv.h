@@ -249,6 +249,30 @@ int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype
               hipEvent_t prof_start, hipEvent_t prof_stop);
 
 /*
+ * sd_verify_noalloc - sd_verify for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, serving loops and harnesses
+ * that forbid allocation.  Same arguments, outputs and results as sd_verify,
+ * without the workspace (and the timing events): the library holds one
+ * workspace of SD_VERIFY_NOALLOC_MAX_WORKSPACE bytes per GPU, a static
+ * device array that each GPU the call runs on keeps until the process ends.
+ * Sizes whose sd_verify_workspace_size(R, gamma_max, V) exceeds it return
+ * SD_ERANGE (R = 256, gamma_max = 11, V = 151936 needs about 3.2 MiB;
+ * R = 512, gamma_max = 16 about 8.9 MiB).  No call allocates, frees or
+ * clears memory: every workspace word a call reads is written earlier in the
+ * same call.  Calls on one GPU share the array, so calls that can overlap
+ * (other streams, other threads) race: serialise them on one stream.
+ * SD_ELAUNCH if the workspace's device address cannot be obtained.
+ */
+#define SD_VERIFY_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+int sd_verify_noalloc(hipStream_t stream, int R, int gamma_max, int V, int ld, int dtype,
+                      float temperature, uint64_t seed, const int64_t* pos0,
+                      const void* tgt_logits, const int32_t* tgt_row0,
+                      const void* drf_logits, const int32_t* drf_row0, const float* drf_stats,
+                      const int32_t* draft_tokens, const int32_t* ell,
+                      int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                      float* probe_probs, float* row_stats, float* accept_prob, int options);
+
+/*
  * sd_markov_draft - semi-autoregressive Markov head plus confidence head
  * [DS innovation one, 2.1; SD move one].
  *

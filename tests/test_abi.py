@@ -117,6 +117,25 @@ def test_markov_host_validation():
     assert _mk(qstats=260) == _lib.SD_EINVAL                        # (m, Z) pairs need 8 bytes
 
 
+def test_verify_noalloc_host_validation():
+    """The allocation-free verify refuses, before any GPU call, sizes whose
+    workspace exceeds the one the library holds (16 MiB per GPU)."""
+    L = sdv.lib()
+    p = ctypes.c_void_p(256)
+    limit = 16 << 20
+    assert sdv.sd_verify_workspace_size(256, 11, 151936) <= limit        # the headline block fits
+    assert sdv.sd_verify_workspace_size(512, 16, 151936) <= limit        # the ragged step fits
+    assert sdv.sd_verify_workspace_size(1024, 64, 151936) > limit
+
+    def call(R, g, V):
+        return L.sd_verify_noalloc(None, R, g, V, V, 1, 1.0, 1, None, p, p, p, p, None, p, p, p, p, p,
+                                   None, None, None, 0)
+    assert call(1024, 64, 151936) == _lib.SD_ERANGE
+    assert call(-1, 4, 1024) == _lib.SD_EINVAL
+    assert call(4, 256, 1024) == _lib.SD_EUNSUPPORTED
+    assert call(0, 4, 1024) == _lib.SD_OK
+
+
 def test_uniforms_host_validation():
     L = sdv.lib()
     p = ctypes.c_void_p(256)
