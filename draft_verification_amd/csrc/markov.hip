@@ -89,59 +89,72 @@ __global__ __launch_bounds__(kThreads) void k_hidden_dot(const uint16_t* __restr
 //
 // The loads are pipelined by specialised waves.  One workgroup per CU walks
 // the 128-column tiles t = blockIdx.x, + gridDim.x, ... (so that at any time
-// the chip sweeps C_k and U_k as one contiguous front) in 64-column stages;
-// four loader waves copy each stage's C rows and U tile
-// from HBM straight into LDS (global_load_lds, 16 bytes per lane, no
-// registers) two stages ahead of eight compute waves, and every wave meets
-// once per stage at a barrier.  A loader wave issues only these copies, so its
-// vmcnt counts them in order and "all but the newest stage done" is an exact
+// the chip sweeps C_k and U_k as one contiguous front) in 64-column stages.
+// Four loader waves copy each stage's 64 C rows from HBM straight into LDS
+// (global_load_lds, 16 bytes per lane, no registers) three stages ahead of
+// eight compute waves, in a ring of four, and every wave meets once per
+// stage at a barrier.  A loader wave issues only these copies, so its vmcnt
+// counts them in order and "all but the newest two stages done" is an exact
 // wait.  Compute wave w owns requests [m0 + 16w, m0 + 16w + 16) and keeps
-// their A rows (the B operand) in registers for the whole step; the product is
-// taken transposed, G^T = C rows . A^T, so that accumulator register i of lane
-// l holds vocabulary 16mb + 4(l/16) + i of request l%16 and the epilogue reads
-// U and writes L straight from registers.
+// their A rows (the B operand) in registers for the whole step; it loads its
+// own part of each U tile straight into registers two stages ahead (U is
+// read once, by the lane that adds it).  The product is taken transposed,
+// G^T = C rows . A^T, with the C rows of a stage assigned to the four 16-row
+// MFMA blocks so that lane l holds, in its 16 accumulators, the vocabulary
+// columns [8q, 8q + 8) and [32 + 8q, 32 + 8q + 8) of the stage for request
+// l % 16 (q = l / 16): each lane reads U and writes L as two 16-byte
+// vectors, and four lanes cover a request's 64 contiguous bytes per store.
 //
 // LDS per stage: C rows [64][kdim] bf16 with the 16-byte chunks of row j
-// XOR-swizzled by the low bits of j (conflict-free fragment reads), then the U
-// tile [128 requests][64] bf16 with chunks swizzled by request.
+// XOR-swizzled (c_swz) so that the sixteen rows one fragment read touches
+// land on distinct chunk columns.
 constexpr int kWsCompute = 8;
 constexpr int kWsLoaders = 4;
 constexpr int kWsThreads = (kWsCompute + kWsLoaders) * 64;
 constexpr int kSubN = 64;
-constexpr int kStages = 3;
-constexpr int kStageC = kSubN * kMaxRank * 2;
-constexpr int kStageU = kTileM * kSubN * 2;
-constexpr int kStageBytes = kStageC + kStageU;
-constexpr int kWsLds = kStages * kStageBytes;
+constexpr int kStages = 4;                       // LDS ring of C stages
+constexpr int kAhead = kStages - 1;              // stages in flight ahead of the one consumed
+constexpr int kStageC = kSubN * kMaxRank * 2;    // 32 KB at the largest rank
+constexpr int kWsLds = kStages * kStageC;
 static_assert(kWsCompute * 16 == kTileM, "one 16-request block per compute wave");
-static_assert(kStageU == 4 * kWsLoaders * 1024, "four 1 KB copies per loader wave for U");
+static_assert(kSubN == 64, "four 16-row MFMA blocks per stage");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Cache-policy operand of global_load_lds on gfx950: the nt bit.
+constexpr int kCPolNonTemporal = 2;
 
 // s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left alone).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  switch (n) {  // kb + 4 copies per stage, kb = kdim / 32 in 1..8
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    default: wait_vmcnt<0>(); break;
+// vmcnt(n) for n = copies a loader wave may leave outstanding: a multiple of
+// kb = kdim / 32 (1..8) copies per stage, at most kAhead - 1 stages.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n == N) wait_vmcnt<N>();
+    else wait_vmcnt_upto<N - 1>(n);
   }
 }
+__device__ __forceinline__ void wait_vmcnt_rt(int n) { wait_vmcnt_upto<8 * (kAhead - 1)>(n); }
 
-// Chunk swizzle of the C rows: XOR with the low bits of the row, within the
-// largest power-of-two group (at most 16) that divides the chunks per row.
+// Stage row of the C fragment that lane rl of MFMA block mb supplies: the
+// block's output row 4q + i then holds vocabulary column
+// 32 (mb / 2) + 8q + 4 (mb % 2) + i of the stage.
+__device__ __forceinline__ int c_row(int mb, int rl) {
+  return 32 * (mb >> 1) + 8 * (rl >> 2) + 4 * (mb & 1) + (rl & 3);
+}
+
+// Chunk swizzle of the C rows: XOR with bits 0-1 and 3-4 of the row (the
+// bits that tell apart the sixteen rows of one fragment read), limited to
+// the largest power of two (at most 16) that divides the chunks per row.
 __device__ __forceinline__ int c_swz(int row, int cpr) {
   const int p2 = cpr & -cpr;
-  return row & ((p2 < 16 ? p2 : 16) - 1);
+  return ((row & 3) | (((row >> 3) & 3) << 2)) & ((p2 < 16 ? p2 : 16) - 1);
 }
 
 // 32-element K slices of the A rows a compute wave keeps: rank <= kMaxRank
@@ -165,47 +178,45 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
   // stages of this workgroup: two per tile it owns
   const int my_tiles = blockIdx.x < n_tiles ? (n_tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int H = 2 * my_tiles;
+  auto stage_col = [&](int h) {  // first vocabulary column of stage h
+    return (blockIdx.x + (h >> 1) * gridDim.x) * kTileN + (h & 1) * kSubN;
+  };
+
+  // Cache policy of the C copies: the Markov head's C_k serves one step, so
+  // it streams past the caches (non-temporal); the RNN head's readout C is
+  // the same at every step and keeps the default policy, under which
+  // repeated steps find it in the last-level cache.  U is read once: always
+  // non-temporal.
+  constexpr int kCPolicy = NSPLIT == 1 ? kCPolNonTemporal : 0;
 
   if (wave >= kWsCompute) {
     // ---------------- loader waves ----------------
-    // Stage h is copied two stages ahead of its use; "stage h+1 landed" is
-    // "at most one stage's copies outstanding" because a loader wave issues
-    // nothing else.
+    // Stage h is copied kAhead stages ahead of its use into ring slot
+    // h % kStages; "stage h+1 landed" is "at most the copies of the stages
+    // issued after it outstanding", since a loader wave issues nothing else.
     const int lw = wave - kWsCompute;
-    const int group = kb + 4;  // copies per stage per loader wave
     auto issue = [&](int h) {
-      const int t = blockIdx.x + (h >> 1) * gridDim.x;
-      const int v0 = t * kTileN + (h & 1) * kSubN;
-      unsigned char* st = lds + (h % kStages) * kStageBytes;
+      const int v0 = stage_col(h);
+      unsigned char* st = lds + (h % kStages) * kStageC;
       for (int ic = 0; ic < kb; ++ic) {  // C rows v0 .. v0+63
         const int region = ic * kWsLoaders + lw;
         const int sid = region * 64 + lane;
         const int row = sid / cpr, ch = (sid % cpr) ^ c_swz(row, cpr);
         const int v = min(v0 + row, V - 1);
         __builtin_amdgcn_global_load_lds((const void*)(Ck + (size_t)v * kdim + ch * 8),
-                                         (lds_void_t*)(st + region * 1024), 16, 0, 0);
-      }
-      for (int iu = 0; iu < 4; ++iu) {  // U tile: 128 requests x 64 columns
-        const int region = iu * kWsLoaders + lw;
-        const int sid = region * 64 + lane;
-        const int req = sid >> 3, ch = (sid & 7) ^ (req & 7);
-        const int r = min(m0 + req, R - 1);
-        const int v = v0 + ch * 8 < V ? v0 + ch * 8 : 0;
-        __builtin_amdgcn_global_load_lds((const void*)(U + ((size_t)r * gamma + (k - 1)) * V + v),
-                                         (lds_void_t*)(st + kStageC + region * 1024), 16, 0, 0);
+                                         (lds_void_t*)(st + region * 1024), 16, 0, kCPolicy);
       }
     };
-    if (H > 0) issue(0);
-    if (H > 1) issue(1);
-    if (H > 1) wait_vmcnt_rt(group); else wait_vmcnt<0>();  // stage 0 landed
+    const int first = H < kAhead ? H : kAhead;
+    for (int h = 0; h < first; ++h) issue(h);
+    wait_vmcnt_rt((first - 1 > 0 ? first - 1 : 0) * kb);  // stage 0 landed
     __builtin_amdgcn_s_barrier();
     for (int h = 0; h < H; ++h) {
-      if (h + 2 < H) {
-        issue(h + 2);
-        wait_vmcnt_rt(group);  // stage h+1 landed (h+2 may still be in flight)
-      } else {
-        wait_vmcnt<0>();
-      }
+      if (h + kAhead < H) issue(h + kAhead);
+      // stage h+1 landed: the stages issued after it may be outstanding
+      const int last = (h + kAhead < H ? h + kAhead : H - 1);
+      const int after = last - (h + 1);
+      wait_vmcnt_rt(after > 0 ? after * kb : 0);
       __builtin_amdgcn_s_barrier();
     }
     return;
@@ -217,9 +228,19 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
   const int r = m0 + req;
   const bool rvalid = r < R;
   const size_t urow = ((size_t)(rvalid ? r : 0) * gamma + (k - 1)) * V;
+  // this lane's U vectors of stage h: columns [8q, 8q+8) and [32+8q, 32+8q+8)
+  auto load_u = [&](int h, uint4 (&u)[2]) {
+    const int v0 = stage_col(h);
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      const int col = v0 + 32 * hv + 8 * q;
+      u[hv] = (rvalid && col < V) ? sdv::ld_nt(U + urow + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 ua[2], ub[2], uc[2];  // U of three consecutive stages
   constexpr int kKs = kHeadKs<NSPLIT>;
   uint4 agf[NSPLIT][kKs];
-  if (A != nullptr) {  // Markov: gather A_k[x_{k-1}] here, under the first stage's load
+  if (A != nullptr) {  // Markov: gather A_k[x_{k-1}] here, under the first stages' loads
     const int x = rvalid ? (k == 1 ? x0[r] : tokens[(size_t)r * gamma + (k - 2)]) : -1;
     const bool xv = x >= 0 && x < V;  // no bias for an invalid token
     const uint16_t* arow = A + ((size_t)(k - 1) * V + (xv ? x : 0)) * kdim;
@@ -235,12 +256,24 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
                           ? *(const uint4*)(Ag + (size_t)r * NSPLIT * kdim + (sp * kb + ks) * 32 + q * 8)
                           : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();  // stage 0 landed
+  // The A rows are in before any U load is issued: every later wait for
+  // vector memory is then for U alone, counted exactly across the loop.
+  wait_vmcnt<0>();
+  if (H > 0) load_u(0, ua);
+  if (H > 1) load_u(1, ub);
+  // The compute waves meet the loaders at plain barriers: the loaders have
+  // waited for their copies before arriving, and a compute wave's LDS reads
+  // of a stage are complete once its MFMAs have consumed them, so no memory
+  // fence is needed (one would also wait for the U loads still in flight).
+  __builtin_amdgcn_s_barrier();  // stage 0 landed
   float pm = kNegInf, ps = 0.0f;  // the first half's partial of the current tile
-  for (int h = 0; h < H; ++h) {
+
+  // Stage h: the product from the C rows in LDS, then the epilogue from the
+  // lane's U vectors u; ends at the barrier that frees the stage's slot.
+  auto stage = [&](int h, const uint4 (&u)[2]) {
     const int t = blockIdx.x + (h >> 1) * gridDim.x;
-    const int v0 = t * kTileN + (h & 1) * kSubN;
-    const unsigned char* st = lds + (h % kStages) * kStageBytes;
+    const int v0 = stage_col(h);
+    const unsigned char* st = lds + (h % kStages) * kStageC;
     floatx4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -250,7 +283,7 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
         uint4 a[4];  // the four row blocks' fragments, read together
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          const int row = mb * 16 + rl;
+          const int row = c_row(mb, rl);
           const int ch = (ks * 4 + q) ^ c_swz(row, cpr);
           a[mb] = *(const uint4*)(st + (row * cpr + ch) * 16);
         }
@@ -262,31 +295,32 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
                                                               acc[mb], 0, 0, 0);
       }
     }
-    // epilogue: L = bf16(U + G) for vocabulary v0 + 16mb + 4q .. +3 of request r
-    uint2 us[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int col = mb * 16 + q * 4;
-      const int ch = (col >> 3) ^ (req & 7);
-      us[mb] = *(const uint2*)(st + kStageC + (req * 8 + ch) * 16 + (col & 7) * 2);
-    }
-    float vals[4][4];
+    // epilogue: L = bf16(U + G); vector hv holds blocks 2hv (columns +0..3)
+    // and 2hv + 1 (columns +4..7) of columns v0 + 32hv + 8q
     float m = kNegInf;
+    float vals[2][8];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int col = mb * 16 + q * 4;
-      const uint2 u = us[mb];
-      uint2 o;
-      o.x = pack_bf16_rne(sdv::bf16lo(u.x) + acc[mb][0], sdv::bf16hi(u.x) + acc[mb][1]);
-      o.y = pack_bf16_rne(sdv::bf16lo(u.y) + acc[mb][2], sdv::bf16hi(u.y) + acc[mb][3]);
-      vals[mb][0] = sdv::bf16lo(o.x);
-      vals[mb][1] = sdv::bf16hi(o.x);
-      vals[mb][2] = sdv::bf16lo(o.y);
-      vals[mb][3] = sdv::bf16hi(o.y);
-      if (rvalid && v0 + col < V) {
-        *(uint2*)(q_logits + urow + v0 + col) = o;
+    for (int hv = 0; hv < 2; ++hv) {
+      const int col = v0 + 32 * hv + 8 * q;
+      const floatx4 g0 = acc[2 * hv], g1 = acc[2 * hv + 1];
+      const uint4 uu = u[hv];
+      uint4 o;
+      o.x = pack_bf16_rne(sdv::bf16lo(uu.x) + g0[0], sdv::bf16hi(uu.x) + g0[1]);
+      o.y = pack_bf16_rne(sdv::bf16lo(uu.y) + g0[2], sdv::bf16hi(uu.y) + g0[3]);
+      o.z = pack_bf16_rne(sdv::bf16lo(uu.z) + g1[0], sdv::bf16hi(uu.z) + g1[1]);
+      o.w = pack_bf16_rne(sdv::bf16lo(uu.w) + g1[2], sdv::bf16hi(uu.w) + g1[3]);
+      vals[hv][0] = sdv::bf16lo(o.x);
+      vals[hv][1] = sdv::bf16hi(o.x);
+      vals[hv][2] = sdv::bf16lo(o.y);
+      vals[hv][3] = sdv::bf16hi(o.y);
+      vals[hv][4] = sdv::bf16lo(o.z);
+      vals[hv][5] = sdv::bf16hi(o.z);
+      vals[hv][6] = sdv::bf16lo(o.w);
+      vals[hv][7] = sdv::bf16hi(o.w);
+      if (rvalid && col < V) {  // V % 8 == 0: a vector is all in or all out
+        *(uint4*)(q_logits + urow + col) = o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, vals[mb][i]);
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, vals[hv][i]);
       }
     }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
@@ -294,10 +328,10 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
     const float ref = exp_ref(m, c);
     float s = 0.0f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (rvalid && v0 + mb * 16 + q * 4 < V) {
+    for (int hv = 0; hv < 2; ++hv) {
+      if (rvalid && v0 + 32 * hv + 8 * q < V) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s += sdv::fast_exp2(fmaf(vals[mb][i], c, -ref));
+        for (int i = 0; i < 8; ++i) s += sdv::fast_exp2(fmaf(vals[hv][i], c, -ref));
       }
     }
     s += __shfl_xor(s, 16, 64);
@@ -313,7 +347,22 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
       if (s != 0.0f) S += s * sdv::fast_exp2(ref - REF);
       partial[(size_t)r * n_tiles + t] = make_float2(M, S);
     }
-    __syncthreads();  // this stage is consumed; the loaders may refill it
+    __builtin_amdgcn_s_barrier();  // this stage is consumed; the loaders may refill its slot
+  };
+
+  // three stages per trip, so that the U vectors rotate through named
+  // registers (each loaded two stages before its use)
+  for (int h = 0; h < H; h += 3) {
+    if (h + 2 < H) load_u(h + 2, uc);
+    stage(h, ua);
+    if (h + 1 < H) {
+      if (h + 3 < H) load_u(h + 3, ua);
+      stage(h + 1, ub);
+    }
+    if (h + 2 < H) {
+      if (h + 4 < H) load_u(h + 4, ub);
+      stage(h + 2, uc);
+    }
   }
 }
 
