@@ -16,11 +16,12 @@
 //                    loader waves stream C_k and U_k into LDS ahead of the
 //                    MFMA waves, which gather their rows A_k[x_{k-1}] while
 //                    the first stage loads
-//   k_markov_select  one workgroup per request: confidence of position k,
-//                    combine tile partials, locate the inverse-CDF tile,
-//                    rescan 128 logits, emit x_k (and, when asked, the row's
-//                    (m, Z), which spares the verifier a pass over the row)
-// plus, up front, one k_hidden_dot launch for w_h . h_k of every position.
+//   k_markov_select  one workgroup per request: combine tile partials,
+//                    locate the inverse-CDF tile, rescan 128 logits, emit x_k
+//                    (and, when asked, the row's (m, Z), which spares the
+//                    verifier a pass over the row)
+// plus, after the block, one k_confidence launch for the confidence of every
+// drafted position (it needs x_{k-1}, never anything later in the loop).
 //
 // sd_rnn_draft runs the same loop for the RNN head: k_rnn_init computes s_1,
 // the bias kernel takes the state's three bf16 terms as its A rows against
@@ -53,28 +54,6 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 }
 
 __device__ __forceinline__ float exp_ref(float m, float c) { return m == kNegInf ? 0.0f : m * c; }
-
-// ---------------------------------------------------------------------------
-// hdot[r][k] = w[0:H] . h[r][k]   (one wave per (r, k))
-__global__ __launch_bounds__(kThreads) void k_hidden_dot(const uint16_t* __restrict__ h, int H,
-                                                         const float* __restrict__ w, int rows,
-                                                         float* __restrict__ hdot) {
-  const int wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (wave >= rows) return;
-  const uint4* hp = (const uint4*)(h + (size_t)wave * H);
-  float acc = 0.0f;
-  for (int v = lane; v < H / 8; v += 64) {
-    const uint4 q = hp[v];
-    const float4 w0 = ((const float4*)w)[2 * v];
-    const float4 w1 = ((const float4*)w)[2 * v + 1];
-    acc += sdv::bf16lo(q.x) * w0.x + sdv::bf16hi(q.x) * w0.y + sdv::bf16lo(q.y) * w0.z +
-           sdv::bf16hi(q.y) * w0.w + sdv::bf16lo(q.z) * w1.x + sdv::bf16hi(q.z) * w1.y +
-           sdv::bf16lo(q.w) * w1.z + sdv::bf16hi(q.w) * w1.w;
-  }
-  acc = sdv::wave_sum(acc);
-  if (lane == 0) hdot[wave] = acc;
-}
 
 // ---------------------------------------------------------------------------
 // The bias product G = A . C_k (M = requests, N = vocabulary, K = kdim) with
@@ -420,21 +399,20 @@ __device__ void rnn_next_state(const NextRows& nr, int r, int V, int tok, float 
   }
 }
 
-// Critical path: the tile partials and x_{k-1} (one round trip), the crossing
-// tile's logits and E[x_{k-1}] (a second, overlapped), and for the RNN head
-// the next state (a third).  The confidence, and for the RNN head W s_k, are
-// computed while the tile's logits are in flight.
+// Critical path: the tile partials and x_{k-1} (one round trip), the
+// crossing tile's logits (a second), and for the RNN head the next state (a
+// third); W s_k is computed while the tile's logits are in flight.  Tile
+// masses are taken as the verifier combines its partials: fp32 exponentials
+// of fp32 exponent differences, summed in fp64.  The confidences wait for
+// the end of the block (k_confidence): nothing in the loop needs them.
 template <bool RNN>
 __global__ __launch_bounds__(kThreads) void k_markov_select(
-    int gamma, int k, int V, int H, int rank_e, float c, float inv_t, uint64_t seed,
-    const int64_t* __restrict__ pos0, const int32_t* __restrict__ x0,
-    const uint16_t* __restrict__ E, const float* __restrict__ w,
-    const float* __restrict__ hdot, const float2* __restrict__ partial, int n_tiles,
+    int gamma, int k, int V, float c, float inv_t, uint64_t seed, const int64_t* __restrict__ pos0,
+    const int32_t* __restrict__ x0, const float2* __restrict__ partial, int n_tiles,
     const uint16_t* __restrict__ q_logits, NextRows nr, int32_t* __restrict__ tokens,
-    float2* __restrict__ q_stats, float* __restrict__ conf, int32_t* __restrict__ status) {
+    float2* __restrict__ q_stats, int32_t* __restrict__ status) {
   __shared__ float s_s[kMaxRank];
   __shared__ float s_red[kThreads / 64];
-  __shared__ float s_rede[kThreads / 64];
   __shared__ double s_redd[kThreads / 64];
   __shared__ int s_tile;
   __shared__ double s_tgt;
@@ -452,17 +430,11 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
 #pragma unroll
   for (int i = 0; i < kPre; ++i)
     pre[i] = (i < per && t0 + i < n_tiles) ? pp[t0 + i] : make_float2(kNegInf, 0.0f);
-  auto part = [&](int i) { return i < kPre ? pre[i] : pp[t0 + i]; };
   if constexpr (RNN) {  // the state the next step advances
     for (int i = tid; i < nr.rank; i += kThreads) s_s[i] = nr.state[(size_t)r * nr.rank + i];
   }
-  const bool xvalid = xp >= 0 && xp < V;
   int st = (k == 1) ? 0 : status[r];
-  if (!xvalid) st |= SD_ST_BAD_TOKEN;
-  // the confidence's embedding term, consumed after the tile is found
-  float e = 0.0f;
-  if (xvalid)
-    for (int i = tid; i < rank_e; i += kThreads) e += w[H + i] * sdv::bf16_to_f32(E[(size_t)xp * rank_e + i]);
+  if (!(xp >= 0 && xp < V)) st |= SD_ST_BAD_TOKEN;
 
   // Combine the tile partials.  Thread t owns a contiguous run of tiles.
   float M = kNegInf;
@@ -476,11 +448,17 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float REF = exp_ref(M, c);
   auto tile_mass = [&](float2 q) {
-    return q.y != 0.0f ? (double)q.y * exp2((double)exp_ref(q.x, c) - (double)REF) : 0.0;
+    return q.y != 0.0f ? (double)q.y * (double)sdv::fast_exp2(exp_ref(q.x, c) - REF) : 0.0;
   };
+  double mass[kPre];  // the preloaded tiles' masses, kept for the walk
   double own = 0.0;
-  for (int i = 0; i < per; ++i)
-    if (t0 + i < n_tiles) own += tile_mass(part(i));
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    mass[i] = tile_mass(pre[i]);  // 0 for the padding entries
+    own += mass[i];
+  }
+  for (int i = kPre; i < per; ++i)
+    if (t0 + i < n_tiles) own += tile_mass(pp[t0 + i]);
   const double incl = sdv::wave_incl_scan_d(own, lane);
   if (lane == 63) s_redd[wave] = incl;
   if (tid == 0) { s_tile = -1; s_tok = -1; s_claim = 0x7FFFFFFF; }
@@ -508,16 +486,32 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
     __syncthreads();
     if (tid == s_claim) {
       double cum = excl;
-      for (int i = 0; i < per && t0 + i < n_tiles; ++i) {
-        const float2 q = part(i);
+      bool done = false;
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) {
+        if (!done && i < per && t0 + i < n_tiles) {
+          const double s = mass[i];
+          if (cum + s > target && s > 0.0) {
+            s_tile = t0 + i;
+            s_tgt = target - cum;
+            s_tref = exp_ref(pre[i].x, c);
+            done = true;
+          } else {
+            cum += s;
+          }
+        }
+      }
+      for (int i = kPre; !done && i < per && t0 + i < n_tiles; ++i) {
+        const float2 q = pp[t0 + i];
         const double s = tile_mass(q);
         if (cum + s > target && s > 0.0) {
           s_tile = t0 + i;
           s_tgt = target - cum;
           s_tref = exp_ref(q.x, c);
-          break;
+          done = true;
+        } else {
+          cum += s;
         }
-        cum += s;
       }
     }
     __syncthreads();
@@ -551,19 +545,9 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
       if (idx < V) lg[e2] = sdv::bf16_to_f32(q_logits[rowoff + idx]);
     }
   }
-  // ... while the RNN head multiplies its state and every wave finishes the
-  // confidence of position k:
-  // sigmoid(w_h . h_k + w_e . E[x_{k-1}])
+  // ... while the RNN head multiplies its state
   float ws = 0.0f;
   if constexpr (RNN) ws = rnn_w_times_state(nr, s_s);
-  e = sdv::wave_sum(e);
-  if (lane == 0) s_rede[wave] = e;
-  __syncthreads();
-  if (tid == 0) {
-    float z = hdot[(size_t)r * gamma + (k - 1)];
-    for (int ww = 0; ww < kThreads / 64; ++ww) z += s_rede[ww];
-    conf[(size_t)r * gamma + (k - 1)] = 1.0f / (1.0f + expf(-z));
-  }
   if (bad) {
     if (tid == 0) {
       tokens[(size_t)r * gamma + (k - 1)] = -1;
@@ -574,10 +558,10 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   }
 
   // rescan the tile's logits: weights relative to the tile's own reference,
-  // scaled into the global frame
+  // scaled into the global frame by the factor its mass was taken with
   if (wave == 0 && tile >= 0) {
     const float tref = s_tref;
-    const double scale = exp2((double)tref - (double)REF);
+    const double scale = (double)sdv::fast_exp2(tref - REF);
     const double tgt_in = s_tgt;
     double wv[2];
     int idx[2];
@@ -611,6 +595,39 @@ __global__ __launch_bounds__(kThreads) void k_markov_select(
   if (RNN && k < gamma) rnn_next_state(nr, r, V, tok, ws);
 }
 
+// Confidence head for every drafted position once the block's tokens are
+// known: conf[r][k-1] = sigmoid(w[0:H] . h[r][k-1] + w[H:] . E[x_{k-1}]), with
+// x_0 the anchor and no embedding term for a token outside [0, V) (a
+// position after a failed row).  One wave per (r, k).
+__global__ __launch_bounds__(kThreads) void k_confidence(int rows, int gamma, int V, int H, int rank_e,
+                                                         const uint16_t* __restrict__ h,
+                                                         const uint16_t* __restrict__ E,
+                                                         const float* __restrict__ w,
+                                                         const int32_t* __restrict__ x0,
+                                                         const int32_t* __restrict__ tokens,
+                                                         float* __restrict__ conf) {
+  const int row = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int r = row / gamma, k = row % gamma + 1;
+  const int xp = k == 1 ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
+  const uint4* hp = (const uint4*)(h + (size_t)row * H);
+  float acc = 0.0f;
+  for (int v = lane; v < H / 8; v += 64) {
+    const uint4 q = hp[v];
+    const float4 w0 = ((const float4*)w)[2 * v];
+    const float4 w1 = ((const float4*)w)[2 * v + 1];
+    acc += sdv::bf16lo(q.x) * w0.x + sdv::bf16hi(q.x) * w0.y + sdv::bf16lo(q.y) * w0.z +
+           sdv::bf16hi(q.y) * w0.w + sdv::bf16lo(q.z) * w1.x + sdv::bf16hi(q.z) * w1.y +
+           sdv::bf16lo(q.w) * w1.z + sdv::bf16hi(q.w) * w1.w;
+  }
+  float e = 0.0f;
+  if (xp >= 0 && xp < V)
+    for (int i = lane; i < rank_e; i += 64) e += w[H + i] * sdv::bf16_to_f32(E[(size_t)xp * rank_e + i]);
+  const float z = sdv::wave_sum(acc) + sdv::wave_sum(e);
+  if (lane == 0) conf[row] = 1.0f / (1.0f + expf(-z));
+}
+
 // s_1 = tanh(W s_0 + E_s[x_0]) = tanh(E_s[x_0]) (s_0 = 0; no embedding term for
 // an anchor outside [0, V)), kept in state[r] and written to Ag[r] split.
 __global__ __launch_bounds__(kThreads) void k_rnn_init(int R, int V, int d, const uint16_t* __restrict__ Es,
@@ -627,12 +644,11 @@ __global__ __launch_bounds__(kThreads) void k_rnn_init(int R, int V, int d, cons
   }
 }
 
-// Workspace: hdot [R][gamma] fp32, tile partials [R][n_tiles] float2, and for
-// the RNN head the split state [R][arow = 3d] bf16 and the state [R][d] fp32.
-size_t head_ws_bytes(int R, int gamma, int V, int arow, int d) {
+// Workspace: tile partials [R][n_tiles] float2, and for the RNN head the
+// split state [R][arow = 3d] bf16 and the state [R][d] fp32.
+size_t head_ws_bytes(int R, int, int V, int arow, int d) {
   const size_t n_tiles = ((size_t)V + kTileN - 1) / kTileN;
-  return sdv_align256((size_t)R * gamma * sizeof(float)) +
-         sdv_align256((size_t)R * n_tiles * sizeof(float2)) +
+  return sdv_align256((size_t)R * n_tiles * sizeof(float2)) +
          sdv_align256((size_t)R * arow * sizeof(uint16_t)) +
          sdv_align256((size_t)R * d * sizeof(float));
 }
@@ -650,12 +666,13 @@ int check_head_args(int R, int gamma, int V, int H, int rank_e, float temperatur
 }
 
 // The sequential loop shared by both heads: per step the bias GEMM + epilogue,
-// then the select kernel (which also prepares the next step's rows).
+// then the select kernel (which also prepares the next step's rows); then
+// the confidences of the whole block.
 template <int NSPLIT>
 int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_stride,
              float temperature, uint64_t seed, const int64_t* pos0, const uint16_t* U,
-             const uint16_t* A, const uint16_t* Ct, const int32_t* x0, int H, const uint16_t* E,
-             int rank_e, const float* w, const float* hdot, float2* partial, const NextRows& nr,
+             const uint16_t* A, const uint16_t* Ct, const int32_t* x0, const uint16_t* h, int H,
+             const uint16_t* E, int rank_e, const float* w, float2* partial, const NextRows& nr,
              int32_t* tokens, uint16_t* q_logits, float* q_stats, float* conf, int32_t* status) {
   const float c = sdv::kLog2e / temperature, inv_t = 1.0f / temperature;
   const int n_tiles = (V + kTileN - 1) / kTileN;
@@ -670,10 +687,13 @@ int run_head(hipStream_t stream, int R, int gamma, int V, int kdim, size_t ct_st
                                gamma, k, V, kdim, c, U, Ct, ct_stride, (const uint16_t*)nr.Ag, A, x0,
                                (const int32_t*)tokens, q_logits, partial, n_tiles));
     SDV_TRY_LAUNCH(sdv::launch(k_markov_select<NSPLIT != 1>, dim3(R), dim3(kThreads), 0, stream, gamma,
-                               k, V, H, rank_e, c, inv_t, seed, pos0, x0, E, w, hdot,
-                               (const float2*)partial, n_tiles, (const uint16_t*)q_logits, nr, tokens,
-                               (float2*)q_stats, conf, status));
+                               k, V, c, inv_t, seed, pos0, x0, (const float2*)partial, n_tiles,
+                               (const uint16_t*)q_logits, nr, tokens, (float2*)q_stats, status));
   }
+  const int rows = R * gamma;
+  SDV_TRY_LAUNCH(sdv::launch(k_confidence, dim3((rows + kThreads / 64 - 1) / (kThreads / 64)),
+                             dim3(kThreads), 0, stream, rows, gamma, V, H, rank_e, h, E, w, x0,
+                             (const int32_t*)tokens, conf));
   return SD_OK;
 }
 
@@ -705,19 +725,10 @@ extern "C" int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int 
         (uintptr_t)w) & 15) != 0 || ((uintptr_t)q_stats & 7) != 0)
     return SD_EINVAL;
 
-  const int n_tiles = (V + kTileN - 1) / kTileN;
-  char* p = (char*)workspace;
-  float* hdot = (float*)p;
-  p += sdv_align256((size_t)R * gamma * sizeof(float));
-  float2* partial = (float2*)p;
-  p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
+  float2* partial = (float2*)workspace;
   const NextRows nr{rank, nullptr, nullptr, nullptr, nullptr};  // unused: no recurrent state
-
-  const int rows = R * gamma;
-  SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
-                             rows, hdot));
   return run_head<1>(stream, R, gamma, V, rank, (size_t)V * rank, temperature, seed, pos0, U, A, Ct,
-                     x0, H, E, rank_e, w, hdot, partial, nr, tokens, q_logits, q_stats, conf, status);
+                     x0, h, H, E, rank_e, w, partial, nr, tokens, q_logits, q_stats, conf, status);
 }
 
 extern "C" size_t sd_rnn_draft_workspace_size(int R, int gamma, int V, int d) {
@@ -749,19 +760,14 @@ extern "C" int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, 
 
   const int n_tiles = (V + kTileN - 1) / kTileN;
   char* p = (char*)workspace;
-  float* hdot = (float*)p;
-  p += sdv_align256((size_t)R * gamma * sizeof(float));
   float2* partial = (float2*)p;
   p += sdv_align256((size_t)R * n_tiles * sizeof(float2));
   uint16_t* Ag = (uint16_t*)p;
   p += sdv_align256((size_t)R * 3 * d * sizeof(uint16_t));
   const NextRows nr{d, W, Es, (float*)p, Ag};
 
-  const int rows = R * gamma;
-  SDV_TRY_LAUNCH(sdv::launch(k_hidden_dot, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, h, H, w,
-                             rows, hdot));
   SDV_TRY_LAUNCH(sdv::launch(k_rnn_init, dim3(R), dim3(kThreads), 0, stream, R, V, d, Es, x0, nr.state,
                              nr.Ag));
-  return run_head<3>(stream, R, gamma, V, d, 0, temperature, seed, pos0, U, nullptr, Ct, x0, H, E,
-                     rank_e, w, hdot, partial, nr, tokens, q_logits, q_stats, conf, status);
+  return run_head<3>(stream, R, gamma, V, d, 0, temperature, seed, pos0, U, nullptr, Ct, x0, h, H, E,
+                     rank_e, w, partial, nr, tokens, q_logits, q_stats, conf, status);
 }
