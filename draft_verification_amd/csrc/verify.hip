@@ -471,47 +471,72 @@ __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec 
     double* bs = bsum;
     if constexpr (!SUMS_READY) {
       if (n_blk <= kLdsBlocks) bs = s_bs;
-      uint4 ct[VL], cd[VL];
-      auto load = [&](int b, uint4 (&t)[VL], uint4 (&d)[VL]) {
+      // Blocks wholly inside the row stream through two register buffers in
+      // turn, each block's loads issued before the previous block is
+      // summed.  Their loads are never skipped (a prefetch past the wave's
+      // last block reads the row's first 16 bytes, every lane the same, and
+      // is not used), so the compiler counts the loads in flight exactly and
+      // waits only for the block about to be summed.  The row's last block,
+      // if partial, follows with bounds-checked loads.
+      const int n_full = nvec / kBlkVec;
+      auto load_full = [&](int b, bool use, uint4 (&t)[VL], uint4 (&d)[VL]) {
 #pragma unroll
         for (int k = 0; k < VL; ++k) {
-          const int v = b * kBlkVec + k * 64 + lane;  // v < nvec implies b < n_blk
-          t[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
-          d[k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
+          const int v = use ? b * kBlkVec + k * 64 + lane : 0;
+          t[k] = sdv::ld_nt(tp + v);
+          d[k] = sdv::ld_nt(dq + v);
         }
       };
-      load(wave, ct, cd);
-      for (int b = wave; b < n_blk; b += kFinWaves) {
-        uint4 nt[VL], nd[VL];
-        load(b + kFinWaves, nt, nd);
-        const double acc = sdv::wave_sum_d(block_lane_mass<BF16, VL>(ct, cd, dp));
+      auto sum_block = [&](int b, const uint4 (&t)[VL], const uint4 (&d)[VL]) {
+        const double acc = sdv::wave_sum_d(block_lane_mass<BF16, VL>(t, d, dp));
         if (lane == 0) bs[b] = acc;
+      };
+      uint4 at[VL], ad[VL], bt[VL], bd[VL];
+      load_full(wave, wave < n_full, at, ad);
+      for (int b = wave; b < n_full; b += 2 * kFinWaves) {
+        const int b1 = b + kFinWaves, b2 = b1 + kFinWaves;
+        load_full(b1, b1 < n_full, bt, bd);
+        sum_block(b, at, ad);
+        if (b1 >= n_full) break;
+        load_full(b2, b2 < n_full, at, ad);
+        sum_block(b1, bt, bd);
+      }
+      if (n_blk > n_full && wave == n_full % kFinWaves) {  // the partial last block
 #pragma unroll
         for (int k = 0; k < VL; ++k) {
-          ct[k] = nt[k];
-          cd[k] = nd[k];
+          const int v = n_full * kBlkVec + k * 64 + lane;
+          at[k] = v < nvec ? sdv::ld_nt(tp + v) : ninf;
+          ad[k] = v < nvec ? sdv::ld_nt(dq + v) : ninf;
         }
+        sum_block(n_full, at, ad);
       }
       __syncthreads();  // block sums of every wave visible to the workgroup
     }
 
-    // thread t owns the contiguous run of blocks [t*per, (t+1)*per)
-    const int per = (n_blk + kFinThreads - 1) / kFinThreads;
-    const int b0 = min(tid * per, n_blk), b1 = min(b0 + per, n_blk);
+    // Locate the block where the inverse CDF crosses u * sum(w) within one
+    // wave: lane l owns the contiguous run of blocks [l*per, (l+1)*per).
+    // Every wave takes the same sums in the same order, so all agree on the
+    // total; with mass present wave 0 locates and scans alone, and without
+    // it all waves go on to the draw from p below.
+    const int per = (n_blk + 63) / 64;
+    const int b0 = min(lane * per, n_blk), b1 = min(b0 + per, n_blk);
     double tot = 0.0;
     for (int b = b0; b < b1; ++b) tot += bs[b];
-    const double incl = block_incl_scan(tot, lane, wave, s_w);
-    s_incl[tid] = incl;
-    __syncthreads();
-    const double total = s_incl[kFinThreads - 1];
+    const double incl = sdv::wave_incl_scan_d(tot, lane);
+    const double total = __shfl(incl, 63, 64);
     if (total > 0.0) {
+      if (wave != 0) return;
       target = u * total;
-      if (incl > target) atomicMin(&s_owner, tid);
-      __syncthreads();
-      if (tid == s_owner) {  // walk the run: first block whose running sum passes
-        double acc = tid == 0 ? 0.0 : s_incl[tid - 1];
-        int blk = -1, lastpos = -1;
-        double rem = __builtin_huge_val();
+      // the first lane whose running sum passes the target (lane 63's is the
+      // total, which u < 1 keeps above it) walks its run
+      const unsigned long long passed = __ballot(incl > target);
+      const int owner = passed ? __ffsll((long long)passed) - 1 : 63;
+      const double before = __shfl_up(incl, 1, 64);
+      int blk = -1;
+      double rem = __builtin_huge_val();
+      if (lane == owner) {
+        double acc = lane == 0 ? 0.0 : before;
+        int lastpos = -1;
         for (int b = b0; b < b1; ++b) {
           const double w = bs[b];
           if (w > 0.0) lastpos = b;
@@ -523,35 +548,31 @@ __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec 
           acc += w;
         }
         if (blk < 0) blk = lastpos;  // rounding: last block with mass, its last element
-        s_blk = blk;
-        s_rem = rem;
       }
-      __syncthreads();
-      if (wave == 0) {
-        const int blk = s_blk;
-        if (blk < 0) {  // no block with mass (not reachable when total > 0)
-          if (lane == 0) {
-            out_tok[n] = -1;
-            a.n_accepted[r] = n;
-            a.status[r] = st;
-          }
-          return;
-        }
-        uint4 tv[VL], dv[VL];
-#pragma unroll
-        for (int k = 0; k < VL; ++k) {
-          const int v = blk * kBlkVec + k * 64 + lane;
-          tv[k] = v < nvec ? tp[v] : ninf;
-          dv[k] = v < nvec ? dq[v] : ninf;
-        }
-        int last;
-        int tok = wave_block_scan<BF16, VL>(tv, dv, blk * kBlkVec, dp, s_rem, lane, &last);
-        if (tok == kNone) tok = last;
+      blk = __shfl(blk, owner, 64);
+      rem = __shfl(rem, owner, 64);
+      if (blk < 0) {  // no block with mass (not reachable when total > 0)
         if (lane == 0) {
-          out_tok[n] = tok;
+          out_tok[n] = -1;
           a.n_accepted[r] = n;
           a.status[r] = st;
         }
+        return;
+      }
+      uint4 tv[VL], dv[VL];
+#pragma unroll
+      for (int k = 0; k < VL; ++k) {
+        const int v = blk * kBlkVec + k * 64 + lane;
+        tv[k] = v < nvec ? tp[v] : ninf;
+        dv[k] = v < nvec ? dq[v] : ninf;
+      }
+      int last;
+      int tok = wave_block_scan<BF16, VL>(tv, dv, blk * kBlkVec, dp, rem, lane, &last);
+      if (tok == kNone) tok = last;
+      if (lane == 0) {
+        out_tok[n] = tok;
+        a.n_accepted[r] = n;
+        a.status[r] = st;
       }
       return;
     }
