@@ -10,7 +10,9 @@ throughput table it keeps the full block, B = R * (1 + gamma) = 3072 rows)
 followed by sd_verify on the rows the schedule chose (ell read on the device,
 no host round trip).  Inputs are resident in HBM before timing starts; three
 input sets of 1.79 GB rotate between steps so the 256 MB last-level cache
-cannot serve repeats.
+cannot serve repeats.  After the warm-up steps, untimed steps run for
+CLOCK_SETTLE_S so that the GPU's clocks are up when the K timed steps start;
+the timing events are made without a system-scope fence.
 
 Also reported: the oracle timed on the host's cores on a bounded sample of
 the same step (cpu_baseline); the ragged asynchronous step (R=512,
@@ -32,17 +34,29 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_partials_headline.json")
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence, hip_runtime_api.h
+# after an idle spell (0.1 s is enough) the GPU's clocks take about 20 ms of
+# load to come back up: measured, the first 20 headline steps ran 15 % slow
+# and the next 20 7 %; every timed region starts after this much untimed work
+CLOCK_SETTLE_S = 0.1
 # the bandwidth pass and the headers it is built from
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_amd", "csrc", f)
                   for f in ("row_partials.hip", "verify_common.h", "sdv_common.h")]
 
 
 class HipEvents:
-    """Raw HIP events on the runtime torch already loaded (same soname)."""
+    """Raw HIP events on the runtime torch already loaded (same soname),
+    recorded on the stream the library's kernels run on (torch's current
+    one).  They are created with hipEventDisableSystemFence: a default event
+    makes a system-scope release, whose cache write-back and invalidation
+    added about 8 us to each 311 us headline step when events were recorded
+    between the steps and around the bandwidth pass (measured); these events
+    only take timestamps."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -51,10 +65,45 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
+
+    def record(self, torch, e):
+        if self.hip.hipEventRecord(ctypes.c_void_p(e),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def span_us(self, torch, fn, n):
+        """Mean time of n back-to-back calls fn(0) .. fn(n - 1), after
+        settle(): two events around the whole run."""
+        settle(torch, fn)
+        ev = self.create(2)
+        self.record(torch, ev[0])
+        for i in range(n):
+            fn(i)
+        self.record(torch, ev[1])
+        torch.cuda.synchronize()
+        us = self.elapsed_ms(ev[0], ev[1]) * 1e3 / n
+        self.destroy(ev)
+        return us
+
+    def per_call_us(self, torch, fn, n, prof=None):
+        """Per-call times of n back-to-back calls fn(i, prof_pair) (events
+        between the calls), after settle(); prof_pair is a pair of the 2 * n
+        events in prof, else None."""
+        settle(torch, lambda i: fn(i, None))
+        ev = self.create(n + 1)
+        self.record(torch, ev[0])
+        for i in range(n):
+            fn(i, (prof[2 * i], prof[2 * i + 1]) if prof else None)
+            self.record(torch, ev[i + 1])
+        torch.cuda.synchronize()
+        us = [self.elapsed_ms(ev[i], ev[i + 1]) * 1e3 for i in range(n)]
+        total = self.elapsed_ms(ev[0], ev[n]) * 1e3
+        self.destroy(ev)
+        return us, total
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -179,14 +228,7 @@ def bench_early_stop(sdv, torch, sets, bufs, ws, sws, steps):
         step(i)
     torch.cuda.synchronize()
     blocks = [int(b[0]["batch"].item()) for b in bufs]
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = hip_events().span_us(torch, step, steps) / 1e3
     B = sum(blocks) / len(blocks)
     return {"verify_rows": blocks, "us_per_step": round(ms * 1e3, 1),
             "rows_per_s": round(B / (ms / 1e3), 1),
@@ -200,21 +242,40 @@ def pct(xs):
             "p90": round(float(np.percentile(xs, 90)), 1)}
 
 
-def timed_steps(torch, step, n_sets, warmup, steps, prof=None):
-    """Run `warmup` untimed then `steps` timed calls of step(i, prof_pair),
-    rotating over n_sets input sets; per-step times from events between the
-    steps (on the current stream, where the library's kernels run), and, when
-    prof holds 2 * steps raw HIP events, the bandwidth pass's time per step."""
+_HIP_EVENTS = None
+
+
+def hip_events():
+    global _HIP_EVENTS
+    if _HIP_EVENTS is None:
+        _HIP_EVENTS = HipEvents()
+    return _HIP_EVENTS
+
+
+def settle(torch, fn):
+    """Untimed calls fn(0), fn(1), ... (eight at a time, then a
+    synchronisation) until CLOCK_SETTLE_S has passed: the clocks are up when
+    the timed calls start."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < CLOCK_SETTLE_S:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def timed_steps(torch, hip, step, warmup, steps, prof=None):
+    """Run `warmup` untimed calls of step(i, None), settle, then `steps`
+    timed calls of step(i, prof_pair); per-step times from events between
+    the steps, and, when prof holds 2 * steps events, the bandwidth pass's
+    time per step in them."""
     for i in range(warmup):
         step(i, None)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record()
-    for i in range(steps):
-        step(i, (prof[2 * i], prof[2 * i + 1]) if prof else None)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    us, _ = hip.per_call_us(torch, step, steps, prof)
+    return us
 
 
 def bench_config(sdv, torch, hip, name, n_sets, steps, warmup, graph_steps=False):
@@ -286,30 +347,26 @@ def bench_config(sdv, torch, hip, name, n_sets, steps, warmup, graph_steps=False
         torch.cuda.current_stream().wait_stream(cap)
         for _ in range(max(warmup, 2)):
             graph.replay()
-        torch.cuda.synchronize()
         n_rep = max(10, steps // n_sets)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
-        ev[0].record()
-        for k in range(n_rep):
-            graph.replay()
-            ev[k + 1].record()
-        torch.cuda.synchronize()
-        per = [ev[k].elapsed_time(ev[k + 1]) * 1e3 / n_sets for k in range(n_rep)]
+        per, _ = hip.per_call_us(torch, lambda k, prof: graph.replay(), n_rep)
+        per = [u / n_sets for u in per]
         res["timing"] = (f"{n_rep} replays of a captured graph holding one step of each of the "
-                         f"{n_sets} input sets; percentiles over replays of the per-step mean")
+                         f"{n_sets} input sets, after {CLOCK_SETTLE_S} s of untimed replays; "
+                         f"percentiles over replays of the per-step mean")
         res["us_per_step"] = pct(per)
         mean_us = float(np.mean(per))
         res["rows_per_s"] = round(float(np.mean(rows)) / (mean_us / 1e6), 1)
         res["all_rows_GBps"] = round(float(np.mean(alg)) / (mean_us / 1e6) / 1e9, 1)
         return res
     kev = hip.create(2 * steps)
-    per = timed_steps(torch, step, n_sets, warmup, steps, prof=kev)
+    per = timed_steps(torch, hip, step, warmup, steps, prof=kev)
     k_us = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) * 1e3 for i in range(steps)]
     hip.destroy(kev)
     step_rows = [rows[i % n_sets] for i in range(steps)]
     step_bytes = [alg[i % n_sets] for i in range(steps)]
     achieved = sum(step_bytes) / (sum(k_us) / 1e6) / 1e9
-    res["timing"] = f"{steps} steps after {warmup} warm-up, events between steps"
+    res["timing"] = (f"{steps} steps after {warmup} warm-up steps and {CLOCK_SETTLE_S} s of untimed "
+                     f"steps, events between steps")
     res["us_per_step"] = pct(per)
     res["rows_per_s"] = round(sum(step_rows) / (sum(per) / 1e6), 1)
     res["bandwidth_pass"] = {"achieved_GBps": round(achieved, 1), "peak_GBps": HBM_PEAK_GBS,
@@ -323,7 +380,7 @@ def bench_config(sdv, torch, hip, name, n_sets, steps, warmup, graph_steps=False
 
 def graph_time_us(torch, fn, calls=10, replays=10):
     """Average time of fn() from a captured graph (the calls are shorter than
-    the host's per-call overhead)."""
+    the host's per-call overhead), after settle()."""
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
@@ -334,15 +391,7 @@ def graph_time_us(torch, fn, calls=10, replays=10):
                 fn()
     torch.cuda.current_stream().wait_stream(cap)
     graph.replay()   # the first replay uploads the graph
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(replays):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (calls * replays) * 1e3
+    return hip_events().span_us(torch, lambda i: graph.replay(), replays) / calls
 
 
 def bench_planner(sdv, torch, inp, vo, ell):
@@ -384,16 +433,8 @@ def bench_rnn(sdv, torch, steps):
                                     inp["E"], inp["w"], 1.0, inp["seed"], workspace=ws, out=out)
     for _ in range(2):
         call()
-    torch.cuda.synchronize()
     n = max(3, min(steps, 20))
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
+    ms = hip_events().span_us(torch, lambda i: call(), n) / 1e3
     hbm = (2 * g * V * d + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # C per step + U + L + h
     flops = 2.0 * R * (3 * d) * V * g                                      # three bf16 terms of the state
     return {"workload": f"R={R}, gamma={g}, V={V}, d={d}, H=4096, bf16",
@@ -418,16 +459,8 @@ def bench_markov(sdv, torch, steps, hip):
                                        inp["w"], 1.0, inp["seed"], workspace=ws, out=out)
     for _ in range(2):
         call()
-    torch.cuda.synchronize()
     n = max(3, min(steps, 20))
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
+    ms = hip.span_us(torch, lambda i: call(), n) / 1e3
     hbm = (2 * g * V * rank + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # Ct + U + L + h
     flops = 2.0 * R * rank * V * g
     res = {"workload": f"R={R}, gamma={g}, V={V}, rank={rank}, H=4096, bf16",
@@ -463,13 +496,7 @@ def bench_markov(sdv, torch, steps, hip):
                       inp["seed"] + 1, workspace=vws, out=vo, drf_stats=out["q_stats"])
     for _ in range(2):
         pipeline()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(n):
-        pipeline()
-    e1.record()
-    torch.cuda.synchronize()
-    pms = e0.elapsed_time(e1) / n
+    pms = hip.span_us(torch, lambda i: pipeline(), n) / 1e3
     B = int(so["batch"].item())
     res["pipeline"] = {"ms_per_step": pms, "batch_rows": B,
                        "emitted_tokens": int(vo["n_acc"].sum().item()) + R,
@@ -501,15 +528,7 @@ def sweep(sdv, torch, steps):
                                          workspace=ws, out=vo, stop_at_rejection=lazy)
             for _ in range(3):
                 call()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(n):
-                call()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / n * 1e3
+            us = hip_events().span_us(torch, lambda i: call(), n)
             rows = R * (g + 1)
             res.append({"R": R, "mode": "in rounds" if lazy else "one pass", "us_per_call": round(us, 1),
                         "rows_per_s": round(rows / (us / 1e6), 1),
@@ -519,6 +538,35 @@ def sweep(sdv, torch, steps):
         del inp, ws
         torch.cuda.empty_cache()
     return res
+
+
+def bench_one(sdv, torch, name, steps, warmup):
+    """One of the workloads besides the headline step, as its own object."""
+    hip = hip_events()
+    if name == "ragged":
+        print("ragged asynchronous step", file=sys.stderr, flush=True)
+        rg = bench_config(sdv, torch, hip, "ragged", 3, steps, warmup)
+        rg["workload"] = ("ragged async step: R=512 requests, gamma_r ~ U{1..16}, V=151936 bf16; "
+                          "global argmax on the previous confidences caps the batch, the top K of "
+                          "the current ones fill it, then verification")
+        return rg
+    if name == "mid":
+        print("mid-size step", file=sys.stderr, flush=True)
+        md = bench_config(sdv, torch, hip, "mid", 8, steps, warmup)
+        md["workload"] = "mid step: R=64, gamma=8, V=32000 bf16, global argmax schedule + verification"
+        mdg = bench_config(sdv, torch, hip, "mid", 8, steps, warmup, graph_steps=True)
+        md["graph_replay"] = {k: mdg[k] for k in ("timing", "us_per_step", "rows_per_s", "all_rows_GBps")}
+        return md
+    if name == "tiny":
+        print("tiny step", file=sys.stderr, flush=True)
+        tn = bench_config(sdv, torch, hip, "tiny", 1, steps, warmup, graph_steps=True)
+        tn["workload"] = "tiny step: R=4, gamma=4, V=1024 fp32, global argmax schedule + verification"
+        return tn
+    if name == "markov":
+        print("markov head", file=sys.stderr, flush=True)
+        return bench_markov(sdv, torch, steps, hip)
+    print("rnn head", file=sys.stderr, flush=True)
+    return bench_rnn(sdv, torch, steps)
 
 
 def main():
@@ -534,6 +582,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only time verification alone at R = 16, 64, 256, 1024 (headline distributions, "
                          "full blocks), in one pass and in rounds, then exit")
+    ap.add_argument("--only", choices=("ragged", "mid", "tiny", "markov", "rnn"),
+                    help="only time this workload (as in the full run) and print its object, then "
+                         "exit: one workload per rocprofv3 trace")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device three times (the known-size kernel that "
                          "scales the rocprofv3 byte counters), then exit")
@@ -565,6 +616,9 @@ def main():
     if args.sweep:
         print(json.dumps({"verify_batch_sweep": sweep(sdv, torch, args.steps)}))
         return
+    if args.only:
+        print(json.dumps({args.only: bench_one(sdv, torch, args.only, args.steps, args.warmup)}))
+        return
     print("generating inputs", file=sys.stderr, flush=True)
     # three independent input sets of 1.79 GB each, rotated: no step can be
     # served from the 256 MB last-level cache
@@ -595,23 +649,17 @@ def main():
                       sch["ell"], V, inp["temperature"], inp["seed"], workspace=ws, out=vo,
                       prof_events=prof)
 
-    hip = HipEvents()
+    hip = hip_events()
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
 
     K = args.steps
     kev = hip.create(2 * K)
     print(f"timing {K} steps", file=sys.stderr, flush=True)
-    sev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    sev[0].record()
-    for i in range(K):
-        step(i, prof=(kev[2 * i], kev[2 * i + 1]))
-        sev[i + 1].record()
-    torch.cuda.synchronize()
-    ms_total = sev[0].elapsed_time(sev[K])
-    step_us = [sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(K)]
+    # settle, then K steps with an event between steps and two around the
+    # bandwidth pass of each
+    step_us, total_us = hip.per_call_us(torch, step, K, prof=kev)
+    ms_total = total_us / 1e3
     k_ms = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(K)]
     hip.destroy(kev)
     ms_per_step = ms_total / K
@@ -630,17 +678,7 @@ def main():
         sdv.sd_verify(inp["tgt"], inp["tgt_row0"], inp["drf"], inp["drf_row0"], inp["draft_tokens"],
                       ells[i % len(sets)], V, inp["temperature"], inp["seed"], workspace=ws,
                       out=bufs[i % len(sets)][1])
-    for i in range(2):
-        verify_only(i)
-    torch.cuda.synchronize()
-    v0 = torch.cuda.Event(enable_timing=True)
-    v1 = torch.cuda.Event(enable_timing=True)
-    v0.record()
-    for i in range(K):
-        verify_only(i)
-    v1.record()
-    torch.cuda.synchronize()
-    verify_us = v0.elapsed_time(v1) / K * 1e3
+    verify_us = hip.span_us(torch, verify_only, K)
 
     # the same step with each draft row's (m, Z) handed over by the drafter
     # (the drafting heads' q_stats): the pairs are taken once, untimed, from a
@@ -667,14 +705,7 @@ def main():
         step_ds(i)
     torch.cuda.synchronize()
     same_tokens = all(torch.equal(bufs[i][1]["tokens"], ref_tokens[i]) for i in range(len(sets)))
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for i in range(K):
-        step_ds(i)
-    d1.record()
-    torch.cuda.synchronize()
-    ds_step_us = d0.elapsed_time(d1) / K * 1e3
+    ds_step_us = hip.span_us(torch, step_ds, K)
 
     # the same step reading each request's rows in rounds of positions and
     # stopping at its first rejection (SD_VERIFY_STOP_AT_REJECTION), without
@@ -693,12 +724,7 @@ def main():
             step_lazy(i, with_stats)
         torch.cuda.synchronize()
         same = all(torch.equal(bufs[i][1]["tokens"], ref_tokens[i]) for i in range(len(sets)))
-        d0.record()
-        for i in range(K):
-            step_lazy(i, with_stats)
-        d1.record()
-        torch.cuda.synchronize()
-        lazy[with_stats] = (d0.elapsed_time(d1) / K * 1e3, same)
+        lazy[with_stats] = (hip.span_us(torch, lambda i: step_lazy(i, with_stats), K), same)
 
     # schedule alone (the rest of the step is verification): its kernels are
     # shorter than the host's per-call overhead, so time a captured graph
@@ -714,17 +740,7 @@ def main():
     rbufs = [torch.empty(bytes_launch, dtype=torch.uint8, device=dev)
              for _ in range(2)]
     sink = torch.empty(max(probe.sink_words(bytes_launch), 1), dtype=torch.int32, device=dev)
-    for i in range(4):
-        probe.read(torch, rbufs[i % 2], sink)
-    torch.cuda.synchronize()
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for i in range(20):
-        probe.read(torch, rbufs[i % 2], sink)
-    r1.record()
-    torch.cuda.synchronize()
-    read_us = r0.elapsed_time(r1) / 20 * 1e3
+    read_us = hip.span_us(torch, lambda i: probe.read(torch, rbufs[i % 2], sink), 20)
     del rbufs
     read_gbs = bytes_launch / (read_us / 1e6) / 1e9
     k_avg = float(np.mean(k_ms))
@@ -746,6 +762,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "clock_settle_s": CLOCK_SETTLE_S,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -795,28 +812,13 @@ def main():
         sets = sets[:1]
         del bufs, dstats, ref_tokens, ells
         torch.cuda.empty_cache()
-        print("ragged asynchronous step", file=sys.stderr, flush=True)
-        rg = bench_config(sdv, torch, hip, "ragged", 3, K, args.warmup)
-        rg["workload"] = ("ragged async step: R=512 requests, gamma_r ~ U{1..16}, V=151936 bf16; "
-                          "global argmax on the previous confidences caps the batch, the top K of "
-                          "the current ones fill it, then verification")
-        result["ragged_async"] = rg
+        result["ragged_async"] = bench_one(sdv, torch, "ragged", K, args.warmup)
         torch.cuda.empty_cache()
-        print("mid-size step", file=sys.stderr, flush=True)
-        md = bench_config(sdv, torch, hip, "mid", 8, K, args.warmup)
-        md["workload"] = "mid step: R=64, gamma=8, V=32000 bf16, global argmax schedule + verification"
-        mdg = bench_config(sdv, torch, hip, "mid", 8, K, args.warmup, graph_steps=True)
-        md["graph_replay"] = {k: mdg[k] for k in ("timing", "us_per_step", "rows_per_s", "all_rows_GBps")}
-        result["mid"] = md
-        print("tiny step", file=sys.stderr, flush=True)
-        tn = bench_config(sdv, torch, hip, "tiny", 1, K, args.warmup, graph_steps=True)
-        tn["workload"] = "tiny step: R=4, gamma=4, V=1024 fp32, global argmax schedule + verification"
-        result["tiny"] = tn
+        result["mid"] = bench_one(sdv, torch, "mid", K, args.warmup)
+        result["tiny"] = bench_one(sdv, torch, "tiny", K, args.warmup)
     if not args.no_markov:
-        print("markov head", file=sys.stderr, flush=True)
-        result["markov_draft"] = bench_markov(sdv, torch, K, hip)
-        print("rnn head", file=sys.stderr, flush=True)
-        result["rnn_draft"] = bench_rnn(sdv, torch, K)
+        result["markov_draft"] = bench_one(sdv, torch, "markov", K, args.warmup)
+        result["rnn_draft"] = bench_one(sdv, torch, "rnn", K, args.warmup)
     if not args.no_cpu_baseline:
         print("cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(sets[0], ell_full)
