@@ -66,9 +66,13 @@ __device__ __forceinline__ float exp_ref(float m, float c) { return m == kNegInf
 // fragments; each term holds the next 8 bits of the fp32 significand, so the
 // three carry the state exactly (normal values).
 //
-// The loads are pipelined by specialised waves.  One workgroup per CU walks
-// the 128-column tiles t = blockIdx.x, + gridDim.x, ... (so that at any time
-// the chip sweeps C_k and U_k as one contiguous front) in 64-column stages.
+// The loads are pipelined by specialised waves.  One workgroup per CU takes
+// one 128-column tile per round i, tile i * G + (blockIdx.x + i) % G (G =
+// gridDim.x), in 64-column stages: a round sweeps one contiguous stretch of
+// C_k and U_k, and the offset that grows with i moves each XCD's tiles
+// across the memory.  (Measured: with tile i * G + blockIdx.x, the
+// workgroups of two of the eight XCDs ended 3 to 5 us after the others on
+// every call, and the call took 6 % longer.)
 // Four loader waves copy each stage's 64 C rows from HBM straight into LDS
 // (global_load_lds, 16 bytes per lane, no registers) three stages ahead of
 // eight compute waves, in a ring of four, and every wave meets once per
@@ -154,11 +158,15 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
   const int kb = kdim / 32;
   const int cpr = kdim / 8;  // 16-byte chunks per C row
   const uint16_t* Ck = Ct + (size_t)(k - 1) * ct_stride;
-  // stages of this workgroup: two per tile it owns
-  const int my_tiles = blockIdx.x < n_tiles ? (n_tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
-  const int H = 2 * my_tiles;
+  // the tile of round i; rounds 0 .. last - 1 are whole, round `last` holds
+  // the n_tiles - last * G tiles left (gridDim.x <= n_tiles)
+  const int G = gridDim.x;
+  auto tile_at = [&](int i) { return i * G + ((int)blockIdx.x + i) % G; };
+  const int last = (n_tiles - 1) / G;
+  const int my_tiles = last + (tile_at(last) < n_tiles ? 1 : 0);
+  const int H = 2 * my_tiles;  // two stages per tile
   auto stage_col = [&](int h) {  // first vocabulary column of stage h
-    return (blockIdx.x + (h >> 1) * gridDim.x) * kTileN + (h & 1) * kSubN;
+    return tile_at(h >> 1) * kTileN + (h & 1) * kSubN;
   };
 
   // Cache policy of the C copies: the Markov head's C_k serves one step, so
@@ -173,17 +181,29 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
     // Stage h is copied kAhead stages ahead of its use into ring slot
     // h % kStages; "stage h+1 landed" is "at most the copies of the stages
     // issued after it outstanding", since a loader wave issues nothing else.
+    // A stage is kb * 4 regions of 1 KB (64 lanes x 16 bytes); loader wave
+    // lw copies regions lw, lw + 4, ... .  The stage row and swizzled chunk
+    // of each of its copies are the same in every stage: worked out once.
     const int lw = wave - kWsCompute;
+    int cp_row[kMaxRank / 32], cp_off[kMaxRank / 32];
+#pragma unroll
+    for (int ic = 0; ic < kMaxRank / 32; ++ic) {
+      const int sid = (ic * kWsLoaders + lw) * 64 + lane;
+      const int row = sid / cpr;
+      cp_row[ic] = row;
+      cp_off[ic] = ((sid % cpr) ^ c_swz(row, cpr)) * 8;
+    }
     auto issue = [&](int h) {
       const int v0 = stage_col(h);
       unsigned char* st = lds + (h % kStages) * kStageC;
-      for (int ic = 0; ic < kb; ++ic) {  // C rows v0 .. v0+63
-        const int region = ic * kWsLoaders + lw;
-        const int sid = region * 64 + lane;
-        const int row = sid / cpr, ch = (sid % cpr) ^ c_swz(row, cpr);
-        const int v = min(v0 + row, V - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(Ck + (size_t)v * kdim + ch * 8),
-                                         (lds_void_t*)(st + region * 1024), 16, 0, kCPolicy);
+#pragma unroll
+      for (int ic = 0; ic < kMaxRank / 32; ++ic) {  // C rows v0 .. v0+63
+        if (ic < kb) {
+          const int v = min(v0 + cp_row[ic], V - 1);
+          __builtin_amdgcn_global_load_lds((const void*)(Ck + (size_t)v * kdim + cp_off[ic]),
+                                           (lds_void_t*)(st + (ic * kWsLoaders + lw) * 1024), 16, 0,
+                                           kCPolicy);
+        }
       }
     };
     const int first = H < kAhead ? H : kAhead;
@@ -250,7 +270,7 @@ __global__ __launch_bounds__(kWsThreads) void k_head_bias(
   // Stage h: the product from the C rows in LDS, then the epilogue from the
   // lane's U vectors u; ends at the barrier that frees the stage's slot.
   auto stage = [&](int h, const uint4 (&u)[2]) {
-    const int t = blockIdx.x + (h >> 1) * gridDim.x;
+    const int t = tile_at(h >> 1);
     const int v0 = stage_col(h);
     const unsigned char* st = lds + (h % kStages) * kStageC;
     floatx4 acc[4];
