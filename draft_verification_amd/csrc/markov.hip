@@ -632,18 +632,45 @@ __global__ __launch_bounds__(kThreads) void k_confidence(int rows, int gamma, in
   const int r = row / gamma, k = row % gamma + 1;
   const int xp = k == 1 ? x0[r] : tokens[(size_t)r * gamma + (k - 2)];
   const uint4* hp = (const uint4*)(h + (size_t)row * H);
-  float acc = 0.0f;
-  for (int v = lane; v < H / 8; v += 64) {
-    const uint4 q = hp[v];
-    const float4 w0 = ((const float4*)w)[2 * v];
-    const float4 w1 = ((const float4*)w)[2 * v + 1];
-    acc += sdv::bf16lo(q.x) * w0.x + sdv::bf16hi(q.x) * w0.y + sdv::bf16lo(q.y) * w0.z +
+  const float4* w4 = (const float4*)w;
+  auto dot8 = [](uint4 q, float4 w0, float4 w1) {
+    return sdv::bf16lo(q.x) * w0.x + sdv::bf16hi(q.x) * w0.y + sdv::bf16lo(q.y) * w0.z +
            sdv::bf16hi(q.y) * w0.w + sdv::bf16lo(q.z) * w1.x + sdv::bf16hi(q.z) * w1.y +
            sdv::bf16lo(q.w) * w1.z + sdv::bf16hi(q.w) * w1.w;
+  };
+  // lane sums vectors lane, lane + 64, ... in that order, four loads at a time
+  float acc = 0.0f;
+  int v = lane;
+  for (; v + 3 * 64 < H / 8; v += 4 * 64) {
+    uint4 q[4];
+    float4 wa[4], wb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      q[u] = hp[v + 64 * u];
+      wa[u] = w4[2 * (v + 64 * u)];
+      wb[u] = w4[2 * (v + 64 * u) + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += dot8(q[u], wa[u], wb[u]);
   }
+  for (; v < H / 8; v += 64) acc += dot8(hp[v], w4[2 * v], w4[2 * v + 1]);
   float e = 0.0f;
-  if (xp >= 0 && xp < V)
-    for (int i = lane; i < rank_e; i += 64) e += w[H + i] * sdv::bf16_to_f32(E[(size_t)xp * rank_e + i]);
+  if (xp >= 0 && xp < V) {
+    const uint16_t* er = E + (size_t)xp * rank_e;
+    int i = lane;
+    for (; i + 3 * 64 < rank_e; i += 4 * 64) {
+      uint16_t x[4];
+      float wx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = er[i + 64 * u];
+        wx[u] = w[H + i + 64 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e += wx[u] * sdv::bf16_to_f32(x[u]);
+    }
+    for (; i < rank_e; i += 64) e += w[H + i] * sdv::bf16_to_f32(er[i]);
+  }
   const float z = sdv::wave_sum(acc) + sdv::wave_sum(e);
   if (lane == 0) conf[row] = 1.0f / (1.0f + expf(-z));
 }
