@@ -304,6 +304,8 @@ int sd_verify_noalloc(hipStream_t stream, int R, int gamma_max, int V, int ld, i
  * Degenerate data: an anchor outside [0, V) sets BAD_TOKEN and contributes
  * neither bias nor embedding; a row of L_k with NaN / +inf (NONFINITE) or all
  * -inf (ZERO_Z) yields token -1 at that position (and BAD_TOKEN next).
+ * Alignment: U, A, Ct, q_logits, h and w 16-byte aligned, q_stats 8-byte
+ * aligned, the workspace 256-byte aligned; SD_EINVAL otherwise.
  */
 size_t sd_markov_draft_workspace_size(int R, int gamma, int V, int rank);
 int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
@@ -329,7 +331,7 @@ int sd_markov_draft(hipStream_t stream, int R, int gamma, int V, int rank,
  *   Ct [V][d] bf16: row n is column n of C
  *   U, x0, h, H, E, rank_e, w, outputs as sd_markov_draft
  *   workspace at least sd_rnn_draft_workspace_size(R, gamma, V, d) bytes,
- *   256-byte aligned.
+ *   256-byte aligned; W 16-byte aligned, the rest as sd_markov_draft.
  */
 size_t sd_rnn_draft_workspace_size(int R, int gamma, int V, int d);
 int sd_rnn_draft(hipStream_t stream, int R, int gamma, int V, int d, float temperature,
