@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kThreads = 1024;  // k_sched_select
 constexpr int kWaves = kThreads / 64;
+static_assert((kWaves & (kWaves - 1)) == 0 && kWaves <= 64, "wave results combine in one wave");
 constexpr int kRankThreads = 256;
 constexpr int kRankCand = 16;   // candidates per ranking workgroup
 constexpr int kRankSegs = kRankThreads / kRankCand;
@@ -53,6 +54,12 @@ __device__ __forceinline__ float sts_calibrate(float c, float T) {
   if (c >= 1.0f) return 1.0f;
   const double odds = (1.0 - (double)c) / (double)c;
   return (float)(1.0 / (1.0 + pow(odds, 1.0 / (double)T)));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, int lane) {
@@ -157,14 +164,18 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
   sps_prev = (i0 >= 1 && i0 - 1 < nslots) ? sps[R + i0 - 1] : 0.0f;
   if (tid == 0) { s_count = 0; s_fail = 0x7FFFFFFF; s_above = 0; }
   __syncthreads();
+  // N = the number of candidates: R * gmax without per-request lengths
   int my_count = 0;
   for (int r = tid; r < R; r += kThreads) {
-    my_count += gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
+    if (gamma_r) my_count += sdv::clampi(gamma_r[r], 0, gmax);
     ell_lds[r] = 0;
   }
-  if (my_count) atomicAdd(&s_count, my_count);
+  if (gamma_r) {
+    my_count = wave_sum_i(my_count);
+    if (lane == 0 && my_count) atomicAdd(&s_count, my_count);
+  }
   __syncthreads();
-  const int N = s_count;
+  const int N = gamma_r ? s_count : nslots;
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (i0 + e >= N) key[e] = ~0ull;
@@ -223,23 +234,27 @@ __global__ __launch_bounds__(kThreads) void k_sched_select(
     s_best_n[wave] = best_n;
   }
   __syncthreads();
-  if (tid == 0) {
-    double b = s_best_theta[0];
-    int bn = s_best_n[0];
-    for (int w = 1; w < kWaves; ++w)
-      if (s_best_theta[w] > b || (s_best_theta[w] == b && s_best_n[w] < bn)) {
-        b = s_best_theta[w];
-        bn = s_best_n[w];
-      }
-    int nstar;
-    if (mode == SD_SCHED_EARLY_STOP) nstar = (s_fail == 0x7FFFFFFF) ? N : s_fail - 1;
-    else if (mode == SD_SCHED_GLOBAL_ARGMAX) nstar = bn;
-    else if (mode == SD_SCHED_THRESHOLD) nstar = s_above;
-    else nstar = sdv::clampi(*cap_k, 0, N);
-    s_nstar = nstar;
-    if (batch_out) *batch_out = R + nstar;
-    if (n_sel_out) *n_sel_out = nstar;
-    if (theta_out && nstar == 0) *theta_out = 0.0;
+  if (wave == 0) {
+    // the waves' bests, combined in lanes 0..kWaves-1 by the same rule
+    double b = lane < kWaves ? s_best_theta[lane] : 0.0;
+    int bn = lane < kWaves ? s_best_n[lane] : 0x7FFFFFFF;
+#pragma unroll
+    for (int o = kWaves / 2; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(b, o, 64);
+      const int on = __shfl_xor(bn, o, 64);
+      if (ob > b || (ob == b && on < bn)) { b = ob; bn = on; }
+    }
+    if (lane == 0) {
+      int nstar;
+      if (mode == SD_SCHED_EARLY_STOP) nstar = (s_fail == 0x7FFFFFFF) ? N : s_fail - 1;
+      else if (mode == SD_SCHED_GLOBAL_ARGMAX) nstar = bn;
+      else if (mode == SD_SCHED_THRESHOLD) nstar = s_above;
+      else nstar = sdv::clampi(*cap_k, 0, N);
+      s_nstar = nstar;
+      if (batch_out) *batch_out = R + nstar;
+      if (n_sel_out) *n_sel_out = nstar;
+      if (theta_out && nstar == 0) *theta_out = 0.0;
+    }
   }
   __syncthreads();
   const int nstar = s_nstar;
