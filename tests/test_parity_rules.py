@@ -8,7 +8,7 @@ import pytest
 from oracle import verify as OV
 from oracle.bf16 import round_to_bf16
 from tests.parity_util import (cdf_shift, check_drafted_row_stats, compare_draft_chains, moved_mass,
-                               assert_row_stats, NEAR)
+                               assert_row_stats, NEAR, partings_bound)
 
 
 def _flip(L, idx):
@@ -81,3 +81,20 @@ def test_draft_chain_partings():
     with pytest.raises(AssertionError):
         compare_draft_chains(np.array([[1, 2, 3]]), conf * (1 + 3e-5), ref, [0])
     assert NEAR == 1e-6
+
+
+def test_partings_bound():
+    """At most 0.75 % of the positions compared (rounded up, at least one)
+    may part, each at a draw the parting rule explains.  At full size the
+    heads compare 2025 (Markov) and 1972 (RNN) positions and part at 4 and 8
+    of them; the allowance of 16 and 15 stays within twice the observed rate,
+    where 2 % (41 and 40) would hide a regression to five times it."""
+    assert partings_bound(1) == 1
+    assert partings_bound(20) == 1
+    assert partings_bound(134) == 2
+    assert partings_bound(2025) == 16
+    assert partings_bound(1972) == 15
+    for compared in (50, 260, 1000, 2025, 4096):
+        b = partings_bound(compared)
+        assert b >= 1 and b <= max(1, 0.0075 * compared + 1)
+
