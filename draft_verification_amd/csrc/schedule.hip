@@ -15,9 +15,10 @@
 // Keys are uint64 so that one ascending integer order sorts by survival
 // descending, then request, then position; they are unique.  Two kernels:
 //   k_sched_rank    many workgroups: each rebuilds every key in LDS (one
-//                   thread per request, fp32 products left to right) and
-//                   ranks 16 candidates by counting the smaller keys, 16
-//                   threads per candidate; writes sorted[rank] = key.  Sorting
+//                   thread per request, fp32 products left to right, into a
+//                   padded position-major table) and ranks 16 candidates by
+//                   counting the smaller keys, 16 threads per candidate;
+//                   writes sorted[rank] = key.  Sorting
 //                   by counting is N^2 work, but spread over the whole chip it
 //                   beats any single-CU network for these sizes (N <= 16384).
 //   k_sched_select  one workgroup: the sorted keys in registers, the
@@ -73,59 +74,73 @@ __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, int lane) {
 }
 
 
-// Survival products of request r, fp32 left to right: keys[i] holds conf[i]'s
-// bits on entry and the candidate's key on exit (slots past gamma_r get the
-// largest key).
-__device__ __forceinline__ void request_keys(int r, int gmax, const int32_t* gamma_r,
-                                             uint64_t* keys, float* surv) {
+// Survival products of request r, fp32 left to right, straight from the
+// confidences (recalibrated first when per-position temperatures are given):
+// the key of position j goes to kT[(j-1) * ld + r] (position-major, ld =
+// R + 1 so that neighbouring requests use neighbouring LDS words and the
+// chain's accesses never share a bank); slots past gamma_r get the largest
+// key.  The loads are independent of the chain and issue together; the
+// products are sequential, as their definition is.
+__device__ __forceinline__ void request_keys(int r, int gmax, int ld, const int32_t* gamma_r,
+                                             const float* conf, const float* sts_temp,
+                                             uint64_t* kT, float* surv) {
   const int g = gamma_r ? sdv::clampi(gamma_r[r], 0, gmax) : gmax;
+  const float* cr = conf + (size_t)r * gmax;
   float a = 1.0f;
-  for (int j = 1; j <= gmax; ++j) {
-    const int i = r * gmax + (j - 1);
-    uint64_t key = ~0ull;
-    float out = 0.0f;
-    if (j <= g) {
-      a = a * __uint_as_float((uint32_t)keys[i]);
-      key = make_key(a, r, j);
-      out = a;
+  constexpr int kU = 8;
+  for (int j0 = 1; j0 <= gmax; j0 += kU) {
+    float cv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) cv[u] = (j0 + u <= g) ? cr[j0 + u - 1] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u;
+      if (j > gmax) break;
+      uint64_t key = ~0ull;
+      float out = 0.0f;
+      if (j <= g) {
+        const float cj = sts_temp ? sts_calibrate(cv[u], sts_temp[j - 1]) : cv[u];
+        a = a * cj;
+        key = make_key(a, r, j);
+        out = a;
+      }
+      kT[(j - 1) * ld + r] = key;
+      if (surv) surv[(size_t)r * gmax + (j - 1)] = out;
     }
-    keys[i] = key;
-    if (surv) surv[i] = out;
   }
 }
 
+// Candidates are the R * gmax slots in position-major order, kRankCand per
+// workgroup (candidate c is slot (c / R) * ld + c % R of the table, so the
+// padding adds no workgroup); kRankSegs segments of kRankCand threads count
+// the smaller keys over the whole padded table, segment s reading keys s,
+// s + kRankSegs, ... (the segments' concurrent reads are neighbouring words;
+// a segment's threads read the same word).
 __global__ __launch_bounds__(kRankThreads) void k_sched_rank(
     int R, int gmax, const int32_t* __restrict__ gamma_r, const float* __restrict__ conf,
     const float* __restrict__ sts_temp, float* __restrict__ surv, uint64_t* __restrict__ sorted) {
-  extern __shared__ uint64_t keys[];
+  extern __shared__ uint64_t kT[];
   __shared__ int part[kRankSegs][kRankCand];
   const int tid = threadIdx.x;
-  const int nslots = R * gmax;
+  const int ld = R + 1;
+  const int nkeys = gmax * ld;  // padded table, the padding holds the largest key
   float* my_surv = blockIdx.x == 0 ? surv : nullptr;  // one workgroup writes it
-  if (sts_temp) {
-    for (int i = tid; i < nslots; i += kRankThreads)
-      keys[i] = __float_as_uint(sts_calibrate(conf[i], sts_temp[i % gmax]));
-  } else {
-    for (int i = tid; i < nslots; i += kRankThreads) keys[i] = __float_as_uint(conf[i]);  // coalesced
-  }
-  __syncthreads();
-  for (int r = tid; r < R; r += kRankThreads) request_keys(r, gmax, gamma_r, keys, my_surv);
+  for (int i = tid; i < gmax; i += kRankThreads) kT[i * ld + R] = ~0ull;
+  for (int r = tid; r < R; r += kRankThreads) request_keys(r, gmax, ld, gamma_r, conf, sts_temp, kT, my_surv);
   __syncthreads();
   const int cl = tid % kRankCand, seg = tid / kRankCand;
   const int cand = blockIdx.x * kRankCand + cl;
-  const uint64_t mine = cand < nslots ? keys[cand] : ~0ull;
-  const int len = (nslots + kRankSegs - 1) / kRankSegs;
-  const int i0 = seg * len, i1 = min(nslots, i0 + len);
+  const uint64_t mine = cand < R * gmax ? kT[(cand / R) * ld + cand % R] : ~0ull;
   int cnt = 0;
-  int i = i0;
-  for (; i + 8 <= i1; i += 8) {  // 8 independent LDS loads in flight
+  int i = seg;
+  for (; i + 7 * kRankSegs < nkeys; i += 8 * kRankSegs) {  // 8 independent LDS loads in flight
     uint64_t q[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) q[u] = keys[i + u];
+    for (int u = 0; u < 8; ++u) q[u] = kT[i + u * kRankSegs];
 #pragma unroll
     for (int u = 0; u < 8; ++u) cnt += q[u] < mine ? 1 : 0;
   }
-  for (; i < i1; ++i) cnt += keys[i] < mine ? 1 : 0;
+  for (; i < nkeys; i += kRankSegs) cnt += kT[i] < mine ? 1 : 0;
   part[seg][cl] = cnt;
   __syncthreads();
   if (tid < kRankCand && mine != ~0ull) {
@@ -310,7 +325,7 @@ extern "C" int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32
   uint64_t* sorted = (uint64_t*)workspace;
   const int nslots = R * gamma_max;
   if (nslots > 0) {
-    const size_t lds = (size_t)nslots * sizeof(uint64_t);
+    const size_t lds = (size_t)gamma_max * (R + 1) * sizeof(uint64_t);  // the padded key table
     if (lds > 64 * 1024)
       SDV_TRY_LAUNCH(hipFuncSetAttribute((const void*)k_sched_rank,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
