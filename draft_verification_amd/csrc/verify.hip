@@ -432,8 +432,7 @@ __device__ __forceinline__ void finish_draw(const VerifyArgs& a, int r, DrawRec 
   __shared__ double s_incl[kFinThreads];
   __shared__ double s_bs[kLdsBlocks];
   __shared__ double s_w[kFinWaves];
-  __shared__ int s_owner, s_blk, s_tok, s_last;
-  __shared__ double s_rem;
+  __shared__ int s_owner, s_tok, s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gmax = a.gmax, S = 2 * gmax + 1, V = a.V;
