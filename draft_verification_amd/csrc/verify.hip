@@ -841,17 +841,19 @@ size_t verify_ws_bytes(int R, int gmax, int V) {
 int next_cover(int cover) { return 2 * cover + 2; }
 
 // Draws spread over the chip: at most this many requests (measured: the two
-// extra launches cost more than they save once the requests fill the CUs).
-#ifndef SDV_WIDE_DRAW_MAX_R
-#define SDV_WIDE_DRAW_MAX_R 128
-#endif
-constexpr int kWideDrawMaxR = SDV_WIDE_DRAW_MAX_R;
+// extra launches cost more than they save once the requests fill the CUs),
+// and rows of at least this many residual blocks (measured, graph-replayed
+// steps: V = 1024 fp32 at R = 4, 37.4 us spread against 32.8 us in the
+// request's workgroup; V = 32000 bf16 (32 blocks) at R = 64, 40.4 against
+// 36.9 us; V = 151936 (149 blocks) is faster spread at every R up to 128).
+constexpr int kWideDrawMaxR = 128;
+constexpr int kWideDrawMinBlk = 64;
 
 // The finishing launches of the last round: PHASE is kFused (one round) or
 // kFinal.
 template <bool BF16, int PHASE>
 int launch_finish(hipStream_t stream, int R, const VerifyArgs& a) {
-  if (R <= kWideDrawMaxR && (PHASE == kFused || PHASE == kFinal)) {
+  if (R <= kWideDrawMaxR && a.n_blk >= kWideDrawMinBlk && (PHASE == kFused || PHASE == kFinal)) {
     constexpr int kRec = PHASE == kFused ? kDecide : kFinalRec;
     SDV_TRY_LAUNCH(sdv::launch(k_finish<BF16, kRec>, dim3(R), dim3(kFinThreads), 0, stream, a));
     const int parts = (a.n_blk + kSumBlocks - 1) / kSumBlocks;

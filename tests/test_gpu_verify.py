@@ -120,9 +120,10 @@ def test_verify_vocab_past_the_lds_block_sums():
 
 def test_verify_draws_in_the_request_workgroup():
     """Batches of more than 128 requests make each correction draw inside the
-    request's own finishing workgroup (smaller batches spread the residual
-    sums over the chip): fp32 rows in one pass and in rounds, and bf16 rows
-    past the LDS block sums (V > 2M) on sampled requests."""
+    request's own finishing workgroup (smaller batches of rows of 64 or more
+    residual blocks spread the residual sums over the chip): fp32 rows in one
+    pass and in rounds, and bf16 rows past the LDS block sums (V > 2M) on
+    sampled requests."""
     inp = _to_cuda(verify_inputs(R=130, gmax=3, V=5000, dtype=torch.float32, sigma_t=2.0,
                                  sigma_d=(0.5, 3.0), seed=91))
     _full_check(inp, np.full(130, 3))
@@ -133,11 +134,12 @@ def test_verify_draws_in_the_request_workgroup():
     assert np.all(to_np(gpu["status"]) == 0)
 
 
-@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 151936), (torch.float32, 5000)])
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 151936), (torch.float32, 70000)])
 def test_verify_draws_identical_in_either_path(dtype, V):
     """The first 128 requests of a 129-request batch verified alone (draws
-    spread over the chip) and inside the batch (each draw in its request's
-    workgroup): identical outputs, bit for bit, in one pass and in rounds."""
+    spread over the chip: rows of 149 and 69 residual blocks) and inside the
+    batch (each draw in its request's workgroup): identical outputs, bit for
+    bit, in one pass and in rounds."""
     R, g = 129, 6
     inp = verify_inputs(R=R, gmax=g, V=V, dtype=dtype, sigma_t=3.0, zipf=True, sigma_d=(0.5, 3.0),
                         seed=93, device="cuda")
