@@ -87,7 +87,9 @@ def sts(conf, temps) -> np.ndarray:
                 out[r, j] = 1.0
             else:
                 odds = (1.0 - c) / c        # exp(-logit(c))
-                out[r, j] = np.float32(1.0 / (1.0 + odds ** (1.0 / temps[j])))
+                # a power past the fp64 range is +inf, whose sigmoid is the limit 0
+                with np.errstate(over="ignore"):
+                    out[r, j] = np.float32(1.0 / (1.0 + odds ** (1.0 / temps[j])))
     return out
 
 
