@@ -13,9 +13,11 @@
 //                    bf16 MFMA GEMM (M = requests, N = vocabulary, K = rank),
 //                    fused with + U_k, bf16 rounding, the q_logits store and a
 //                    per-(row, 128-column tile) partial (max, sum 2^(L*c - ref));
-//                    loader waves stream C_k and U_k into LDS ahead of the
-//                    MFMA waves, which gather their rows A_k[x_{k-1}] while
-//                    the first stage loads
+//                    loader waves stream C_k into LDS ahead of the MFMA
+//                    waves, which gather their rows A_k[x_{k-1}] while the
+//                    first stage loads, load their own U_k vectors into
+//                    registers and store L through a small LDS buffer as
+//                    whole cache lines
 //   k_markov_select  one workgroup per request: combine tile partials,
 //                    locate the inverse-CDF tile, rescan 128 logits, emit x_k
 //                    (and, when asked, the row's (m, Z), which spares the
