@@ -21,13 +21,15 @@
 //                   rejected row pair once (16 waves, next block's loads in
 //                   flight) for the sums of max(0, p - q) per 1024-element
 //                   block, locates the block where the inverse CDF crosses
-//                   u * sum(w) with a workgroup prefix sum, and one wave scans
-//                   that block.  A bonus draw locates its chunk from the first
-//                   pass's partials and rescans only that chunk.
-//   k_draw_sums     small batches only (too few requests to fill the CUs):
-//                   k_finish records the draws, this kernel takes the block
-//                   sums with many workgroups per rejected row pair, and a
-//                   last k_finish launch locates and scans as above
+//                   u * sum(w) within one wave (a ballot over the lanes'
+//                   running sums), and that wave scans the block.  A bonus
+//                   draw locates its chunk from the first pass's partials and
+//                   rescans only that chunk.
+//   k_draw_sums     small batches of long rows only (too few requests to fill
+//                   the CUs): k_finish records the draws, this kernel takes
+//                   the block sums with many workgroups per rejected row
+//                   pair, and a last k_finish launch locates and scans as
+//                   above
 //
 // Verification that stops at each request's first rejection runs the
 // bandwidth pass and the deciding half of k_finish in rounds of positions
