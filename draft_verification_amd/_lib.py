@@ -146,14 +146,22 @@ def _on_stream(fn):
     never to another stream while these kernels may still use it.  Outputs
     and workspaces the caller passes in are the caller's to keep alive on
     that stream."""
-    sig = inspect.signature(fn)
+    at = list(inspect.signature(fn).parameters).index("stream")
 
     @functools.wraps(fn)
     def wrapper(*args, **kw):
-        stream = sig.bind_partial(*args, **kw).arguments.get("stream")
+        stream = kw.get("stream") if "stream" in kw else (args[at] if len(args) > at else None)
+        if stream is None:  # torch's current stream already
+            return fn(*args, **kw)
         with torch.cuda.stream(stream):
             return fn(*args, **kw)
     return wrapper
+
+
+def _out(o, key, make):
+    """The caller's output `key` from `o` when present, else a new tensor
+    from make() (made only then)."""
+    return o[key] if key in o else make()
 
 
 def _check(fn, code):
@@ -181,11 +189,11 @@ def sd_schedule(conf, sps, mode, gamma_r=None, cap_k=None, out=None, surv=True, 
     R, gmax = conf.shape
     dev = conf.device
     o = out or {}
-    ell = o.get("ell", torch.empty(R, dtype=torch.int32, device=dev))
-    batch = o.get("batch", torch.empty(1, dtype=torch.int32, device=dev))
-    n_sel = o.get("n_sel", torch.empty(1, dtype=torch.int32, device=dev))
-    theta = o.get("theta", torch.empty(1, dtype=torch.float64, device=dev))
-    sv = o.get("surv", torch.empty((R, gmax), dtype=torch.float32, device=dev)) if surv else None
+    ell = _out(o, "ell", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    batch = _out(o, "batch", lambda: torch.empty(1, dtype=torch.int32, device=dev))
+    n_sel = _out(o, "n_sel", lambda: torch.empty(1, dtype=torch.int32, device=dev))
+    theta = _out(o, "theta", lambda: torch.empty(1, dtype=torch.float64, device=dev))
+    sv = _out(o, "surv", lambda: torch.empty((R, gmax), dtype=torch.float32, device=dev)) if surv else None
     ws = workspace if workspace is not None else _workspace(sd_schedule_workspace_size(R, gmax), dev)
     code = lib().sd_schedule(
         _stream(stream), R, gmax, _ptr(gamma_r, torch.int32, "gamma_r"),
@@ -229,12 +237,12 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
         raise ValueError("target and draft rows must share dtype and leading dimension")
     ld = tgt.shape[1]
     o = out or {}
-    n_acc = o.get("n_acc", torch.empty(R, dtype=torch.int32, device=dev))
-    toks = o.get("tokens", torch.empty((R, gmax + 1), dtype=torch.int32, device=dev))
-    status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
-    pp = o.get("probe", torch.zeros((R, gmax, 2), dtype=torch.float32, device=dev)) if probe else None
-    rs = o.get("row_stats", torch.zeros((R, 2 * gmax + 1, 2), dtype=torch.float32, device=dev)) if stats else None
-    al = o.get("alpha", torch.zeros((R, gmax), dtype=torch.float32, device=dev)) if alpha else None
+    n_acc = _out(o, "n_acc", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    toks = _out(o, "tokens", lambda: torch.empty((R, gmax + 1), dtype=torch.int32, device=dev))
+    status = _out(o, "status", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    pp = _out(o, "probe", lambda: torch.zeros((R, gmax, 2), dtype=torch.float32, device=dev)) if probe else None
+    rs = _out(o, "row_stats", lambda: torch.zeros((R, 2 * gmax + 1, 2), dtype=torch.float32, device=dev)) if stats else None
+    al = _out(o, "alpha", lambda: torch.zeros((R, gmax), dtype=torch.float32, device=dev)) if alpha else None
     wsz = sd_verify_workspace_size(R, gmax, V)
     ws = workspace if workspace is not None else _workspace(wsz, dev)
     code = lib().sd_verify(
@@ -299,11 +307,11 @@ def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, w
     dev = U.device
     bf = torch.bfloat16
     o = out or {}
-    tokens = o.get("tokens", torch.empty((R, gamma), dtype=torch.int32, device=dev))
-    ql = o.get("q_logits", torch.empty((R, gamma, V), dtype=bf, device=dev))
-    conf = o.get("conf", torch.empty((R, gamma), dtype=torch.float32, device=dev))
-    status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
-    qs = o.get("q_stats", torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
+    tokens = _out(o, "tokens", lambda: torch.empty((R, gamma), dtype=torch.int32, device=dev))
+    ql = _out(o, "q_logits", lambda: torch.empty((R, gamma, V), dtype=bf, device=dev))
+    conf = _out(o, "conf", lambda: torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    status = _out(o, "status", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    qs = _out(o, "q_stats", lambda: torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
     wsz = sd_markov_draft_workspace_size(R, gamma, V, rank)
     ws = workspace if workspace is not None else _workspace(wsz, dev)
     code = lib().sd_markov_draft(
@@ -334,11 +342,11 @@ def sd_rnn_draft(U, W, Es, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, 
     dev = U.device
     bf = torch.bfloat16
     o = out or {}
-    tokens = o.get("tokens", torch.empty((R, gamma), dtype=torch.int32, device=dev))
-    ql = o.get("q_logits", torch.empty((R, gamma, V), dtype=bf, device=dev))
-    conf = o.get("conf", torch.empty((R, gamma), dtype=torch.float32, device=dev))
-    status = o.get("status", torch.empty(R, dtype=torch.int32, device=dev))
-    qs = o.get("q_stats", torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
+    tokens = _out(o, "tokens", lambda: torch.empty((R, gamma), dtype=torch.int32, device=dev))
+    ql = _out(o, "q_logits", lambda: torch.empty((R, gamma, V), dtype=bf, device=dev))
+    conf = _out(o, "conf", lambda: torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    status = _out(o, "status", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    qs = _out(o, "q_stats", lambda: torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
     ws = workspace if workspace is not None else _workspace(sd_rnn_draft_workspace_size(R, gamma, V, d),
                                                             dev)
     code = lib().sd_rnn_draft(
@@ -388,14 +396,14 @@ def sd_lightspec_plan(ema, count, d_prev, sps, draft_cost, out=None, workspace=N
     R = d_prev.shape[0]
     dev = ema.device
     o = out or {}
-    conf = o.get("conf", torch.empty(gmax, dtype=torch.float32, device=dev))
-    ell = o.get("ell", torch.empty(R, dtype=torch.int32, device=dev))
-    batch = o.get("batch", torch.empty(1, dtype=torch.int32, device=dev))
-    n_sel = o.get("n_sel", torch.empty(1, dtype=torch.int32, device=dev))
-    theta = o.get("theta", torch.empty(1, dtype=torch.float64, device=dev))
-    d_next = o.get("d_next", torch.empty(1, dtype=torch.int32, device=dev))
-    b_next = o.get("b_next", torch.empty(1, dtype=torch.int32, device=dev))
-    phi = o.get("phi", torch.empty(gmax, dtype=torch.float64, device=dev))
+    conf = _out(o, "conf", lambda: torch.empty(gmax, dtype=torch.float32, device=dev))
+    ell = _out(o, "ell", lambda: torch.empty(R, dtype=torch.int32, device=dev))
+    batch = _out(o, "batch", lambda: torch.empty(1, dtype=torch.int32, device=dev))
+    n_sel = _out(o, "n_sel", lambda: torch.empty(1, dtype=torch.int32, device=dev))
+    theta = _out(o, "theta", lambda: torch.empty(1, dtype=torch.float64, device=dev))
+    d_next = _out(o, "d_next", lambda: torch.empty(1, dtype=torch.int32, device=dev))
+    b_next = _out(o, "b_next", lambda: torch.empty(1, dtype=torch.int32, device=dev))
+    phi = _out(o, "phi", lambda: torch.empty(gmax, dtype=torch.float64, device=dev))
     wsz = lib().sd_lightspec_plan_workspace_size(R, gmax)
     ws = workspace if workspace is not None else _workspace(wsz, dev)
     _check("sd_lightspec_plan", lib().sd_lightspec_plan(
