@@ -243,8 +243,7 @@ def sd_verify(tgt, tgt_row0, drf, drf_row0, draft_tokens, ell, V, temperature=1.
     pp = _out(o, "probe", lambda: torch.zeros((R, gmax, 2), dtype=torch.float32, device=dev)) if probe else None
     rs = _out(o, "row_stats", lambda: torch.zeros((R, 2 * gmax + 1, 2), dtype=torch.float32, device=dev)) if stats else None
     al = _out(o, "alpha", lambda: torch.zeros((R, gmax), dtype=torch.float32, device=dev)) if alpha else None
-    wsz = sd_verify_workspace_size(R, gmax, V)
-    ws = workspace if workspace is not None else _workspace(wsz, dev)
+    ws = workspace if workspace is not None else _workspace(sd_verify_workspace_size(R, gmax, V), dev)
     code = lib().sd_verify(
         _stream(stream), R, gmax, int(V), ld, dt, float(temperature), int(seed) & (2**64 - 1),
         _ptr(pos0, torch.int64, "pos0"), _ptr(tgt, None, "tgt"), _ptr(tgt_row0, torch.int32, "tgt_row0"),
@@ -312,8 +311,7 @@ def sd_markov_draft(U, A, Ct, x0, h, E, w, temperature=1.0, seed=0, pos0=None, w
     conf = _out(o, "conf", lambda: torch.empty((R, gamma), dtype=torch.float32, device=dev))
     status = _out(o, "status", lambda: torch.empty(R, dtype=torch.int32, device=dev))
     qs = _out(o, "q_stats", lambda: torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)) if stats else None
-    wsz = sd_markov_draft_workspace_size(R, gamma, V, rank)
-    ws = workspace if workspace is not None else _workspace(wsz, dev)
+    ws = workspace if workspace is not None else _workspace(sd_markov_draft_workspace_size(R, gamma, V, rank), dev)
     code = lib().sd_markov_draft(
         _stream(stream), R, gamma, V, rank, float(temperature), int(seed) & (2**64 - 1),
         _ptr(pos0, torch.int64, "pos0"), _ptr(U, bf, "U"), _ptr(A, bf, "A"), _ptr(Ct, bf, "Ct"),
@@ -404,8 +402,7 @@ def sd_lightspec_plan(ema, count, d_prev, sps, draft_cost, out=None, workspace=N
     d_next = _out(o, "d_next", lambda: torch.empty(1, dtype=torch.int32, device=dev))
     b_next = _out(o, "b_next", lambda: torch.empty(1, dtype=torch.int32, device=dev))
     phi = _out(o, "phi", lambda: torch.empty(gmax, dtype=torch.float64, device=dev))
-    wsz = lib().sd_lightspec_plan_workspace_size(R, gmax)
-    ws = workspace if workspace is not None else _workspace(wsz, dev)
+    ws = workspace if workspace is not None else _workspace(lib().sd_lightspec_plan_workspace_size(R, gmax), dev)
     _check("sd_lightspec_plan", lib().sd_lightspec_plan(
         _stream(stream), R, gmax, _ptr(ema, torch.float64, "ema"), _ptr(count, torch.int64, "count"),
         _ptr(d_prev, torch.int32, "d_prev"), _ptr(sps, torch.float32, "sps"), sps.numel(),
