@@ -113,6 +113,18 @@ def test_markov_small_full():
     assert parted <= partings_bound(compared)
 
 
+def test_markov_smallest_vocabulary():
+    """V = 8: one tile of which only 8 of the 128 columns exist, so every
+    stage past the first holds no vocabulary column at all."""
+    inp = markov_inputs(R=3, gamma=3, V=8, rank=32, H=8, rank_e=8, sigma_u=1.0, sigma_f=0.3, seed=92,
+                        device="cuda")
+    out = _run(inp)
+    assert np.all(to_np(out["status"]) == 0)
+    ref = oracle_chain(inp, range(3), keep=range(3))
+    compared, parted, _ = check_chain(inp, out, ref, range(3))
+    assert parted <= partings_bound(compared)
+
+
 @pytest.mark.parametrize("rank", [96, 160, 224])
 def test_markov_ranks_off_the_powers_of_two(rank):
     """rank = 32 * 3, 5, 7: C rows of 12, 20, 28 sixteen-byte chunks (the LDS

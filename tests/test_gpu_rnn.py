@@ -106,6 +106,16 @@ def test_rnn_small_full():
     assert parted <= partings_bound(compared)
 
 
+def test_rnn_smallest_vocabulary():
+    """V = 8 and d = 32: one vocabulary tile with 8 live columns."""
+    inp = rnn_inputs(R=3, gamma=3, V=8, d=32, H=8, rank_e=8, sigma_c=0.3, seed=96, device="cuda")
+    out = _run(inp)
+    assert np.all(to_np(out["status"]) == 0)
+    ref = oracle_chain(inp, range(3), keep=range(3))
+    compared, parted, _ = check_chain(inp, out, ref, range(3))
+    assert parted <= partings_bound(compared)
+
+
 @pytest.mark.parametrize("d", [32, 96, 128])
 def test_rnn_state_sizes_and_positions(d):
     inp = rnn_inputs(R=9, gamma=6, V=1000, d=d, H=16, rank_e=8, sigma_c=0.4, seed=96 + d, device="cuda")

@@ -98,6 +98,14 @@ def test_verify_without_drafts():
         assert np.all(to_np(gpu["n_acc"]) == 0)
 
 
+def test_verify_smallest_vocabulary():
+    """V = 8, the smallest the library takes: one 16-byte vector per bf16 row,
+    two per fp32 row, a single chunk and block."""
+    for dtype in (torch.bfloat16, torch.float32):
+        inp = _to_cuda(verify_inputs(R=5, gmax=3, V=8, dtype=dtype, sigma_t=1.5, sigma_d=(0.5, 2.0), seed=84))
+        _full_check(inp, np.array([3, 0, 1, 2, 3]))
+
+
 def test_verify_maximum_draft_length():
     """gamma_max = 255 (the build's limit): 511 batch rows per request and up
     to 255 accept tests at once; drafts close to the target so that long
