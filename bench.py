@@ -141,6 +141,33 @@ class ReadProbe:
         if rc != 0:
             raise RuntimeError(f"probe_stream_read failed: {rc}")
 
+    def mix(self, torch, src, dst, ratio):
+        wbytes = dst.numel() * dst.element_size()
+        assert src.numel() * src.element_size() >= ratio * wbytes
+        self.lib.probe_stream_mix.restype = ctypes.c_int
+        self.lib.probe_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_longlong, ctypes.c_int]
+        rc = self.lib.probe_stream_mix(torch.cuda.current_stream().cuda_stream, src.data_ptr(),
+                                       dst.data_ptr(), wbytes, ratio)
+        if rc != 0:
+            raise RuntimeError(f"probe_stream_mix failed: {rc}")
+
+
+def mixed_ceiling(torch, hip, wbytes, ratio, what):
+    """Practical ceiling of a stream that reads `ratio` bytes per byte it
+    writes: libsdv_probe's plain mixed stream over one drafting position's
+    bytes (wbytes written), three buffer sets rotating so that the last-level
+    cache cannot serve repeats."""
+    probe = ReadProbe()
+    wbytes -= wbytes % 2048
+    sets = [(torch.empty(ratio * wbytes, dtype=torch.uint8, device="cuda"),
+             torch.empty(wbytes, dtype=torch.uint8, device="cuda")) for _ in range(3)]
+    us = hip.span_us(torch, lambda i: probe.mix(torch, sets[i % 3][0], sets[i % 3][1], ratio), 30)
+    del sets
+    gbs = (ratio + 1) * wbytes / (us / 1e6) / 1e9
+    return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "read_per_write": ratio,
+            "us_per_position": round(us, 2), "what": what}
+
 
 def source_hash():
     h = hashlib.sha256()
@@ -437,11 +464,14 @@ def bench_rnn(sdv, torch, steps):
     ms = hip_events().span_us(torch, lambda i: call(), n) / 1e3
     hbm = (2 * g * V * d + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # C per step + U + L + h
     flops = 2.0 * R * (3 * d) * V * g                                      # three bf16 terms of the state
+    ceil = mixed_ceiling(torch, hip_events(), 2 * R * V, 2,
+                         "plain stream of one position's bytes: C and U_k read, L_k written")
+    ceil["call_frac_of_ceiling"] = round(hbm / (ms / 1e3) / ceil["GBps"], 4)
     return {"workload": f"R={R}, gamma={g}, V={V}, d={d}, H=4096, bf16",
             "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
             "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
             "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
-            "launches": 2 * g + 2}
+            "launches": 2 * g + 2, "mixed_ceiling": ceil}
 
 
 def bench_markov(sdv, torch, steps, hip):
@@ -463,11 +493,14 @@ def bench_markov(sdv, torch, steps, hip):
     ms = hip.span_us(torch, lambda i: call(), n) / 1e3
     hbm = (2 * g * V * rank + 2 * R * g * V * 2 + 2 * R * g * 4096) / 1e9   # Ct + U + L + h
     flops = 2.0 * R * rank * V * g
+    ceil = mixed_ceiling(torch, hip, 2 * R * V, 3,
+                         "plain stream of one position's bytes: C_k and U_k read, L_k written")
+    ceil["call_frac_of_ceiling"] = round(hbm / (ms / 1e3) / ceil["GBps"], 4)
     res = {"workload": f"R={R}, gamma={g}, V={V}, rank={rank}, H=4096, bf16",
            "ms_per_call": ms, "hbm_GBps": hbm / (ms / 1e3), "hbm_frac": hbm / (ms / 1e3) / HBM_PEAK_GBS,
            "mfma_TFLOPs": flops / (ms / 1e3) / 1e12,
            "mfma_frac": flops / (ms / 1e3) / 1e12 / BF16_DENSE_TFLOPS,
-           "launches": 2 * g + 2}
+           "launches": 2 * g + 2, "mixed_ceiling": ceil}
 
     # one whole step at these sizes: draft, schedule (early stop) on the
     # drafted confidences, verify the drafted rows against target rows with
