@@ -100,6 +100,24 @@ def test_schedule_sizes_around_the_select_layouts(R, gmax):
         _check(conf, sps, OS.THRESHOLD, gam, threshold=0.3)
 
 
+@pytest.mark.parametrize("R,gmax", [(1024, 1), (1025, 1), (4, 255), (1, 255), (5, 205), (33, 31)])
+def test_schedule_long_chains_and_single_drafts(R, gmax):
+    """The longest chains (gamma_max = 255, 205) next to wide batches of
+    single drafts, around one candidate per selection thread (1024, 1025),
+    with ragged lengths, tied survivals and per-position temperatures."""
+    g = np.random.default_rng(R * 1000 + gmax)
+    conf = (1 / (1 + np.exp(-g.normal(2.0, 1.5, (R, gmax))))).astype(np.float32)
+    conf[:, ::3] = np.float32(0.75)                  # repeated values: tied survivals
+    gam = g.integers(0, gmax + 1, R).astype(np.int32)
+    sts = (0.5 + g.random(gmax)).astype(np.float32)
+    sps = sps_table(R * (gmax + 1), 256, 0.08, 64).numpy()
+    for mode in MODES:
+        _check(conf, sps, mode, gam)
+        _check(conf, sps, mode, sts=sts)
+    _check(conf, sps, OS.CAPPED_TOPK, gam, cap=int(g.integers(0, R * gmax + 3)), sts=sts)
+    _check(conf, sps, OS.THRESHOLD, gam, threshold=0.3)
+
+
 def test_schedule_maximum_slots_and_subnormal_survival():
     g = np.random.default_rng(13)
     R, gmax = 1024, 16                          # R * gmax = 16384, the limit
