@@ -28,12 +28,15 @@ template <bool BF16>
 __device__ __forceinline__ void row_chunk(const sdv::RowPassArgs& a, int r, int slot, int ch) {
   using VT = sdv::Vec<BF16>;
   constexpr int kVec = kChunk / VT::kElems / kRowThreads;
+  // the row's first index is requested with the request's length (one
+  // round trip for both: the exit test reads it too, so it is not deferred
+  // past the test); a negative one names no row and is skipped
+  const int row0 = slot <= a.gmax ? a.tgt_row0[r] : a.drf_row0[r];
   const int L = sdv::clampi(a.ell[r], 0, a.gmax);
-  if (!sdv::slot_in_batch(slot, a.gmax, L)) return;
+  if (!sdv::slot_in_batch(slot, a.gmax, L) || row0 < 0) return;
   const int rs = r * (2 * a.gmax + 1) + slot;  // row of the partials' layout
-  const char* row = slot <= a.gmax
-                        ? a.tgt + ((int64_t)a.tgt_row0[r] + slot) * a.ld_bytes
-                        : a.drf + ((int64_t)a.drf_row0[r] + (slot - a.gmax - 1)) * a.ld_bytes;
+  const char* row = slot <= a.gmax ? a.tgt + ((int64_t)row0 + slot) * a.ld_bytes
+                                   : a.drf + ((int64_t)row0 + (slot - a.gmax - 1)) * a.ld_bytes;
   const int e0 = ch * kChunk;
   const int nvec = min(kChunk, a.V - e0) / VT::kElems;
   const uint4* p = (const uint4*)(row + (int64_t)e0 * VT::kBytes);

@@ -176,7 +176,9 @@ int sd_schedule(hipStream_t stream, int R, int gamma_max, const int32_t* gamma_r
  *   ld >= V, ld % 8 == 0; dtype SD_DTYPE_F32 or SD_DTYPE_BF16; temperature > 0
  *   pos0        [R] int64 or NULL (all 0)
  *   tgt_logits, drf_logits   row-major logit rows (dtype), see above
- *   tgt_row0, drf_row0       [R] int32 first row of each request
+ *   tgt_row0, drf_row0       [R] int32 first row of each request, >= 0, with
+ *                            every row it names inside its buffer (device
+ *                            values, not checked)
  *   drf_stats    [R][gamma_max][2] fp32 or NULL: (m, Z) of the draft row of
  *                each position j = 1..gamma_max, in row_stats' format below.
  *                The drafter normalised q_j when it sampled x_j, so it can
