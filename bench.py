@@ -130,6 +130,9 @@ class ReadProbe:
         self.lib.probe_stream_read.restype = ctypes.c_int
         self.lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
                                                ctypes.c_void_p]
+        self.lib.probe_stream_mix.restype = ctypes.c_int
+        self.lib.probe_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_longlong, ctypes.c_int]
 
     def sink_words(self, nbytes):
         return int(self.lib.probe_stream_read_sink_words(nbytes))
@@ -144,9 +147,6 @@ class ReadProbe:
     def mix(self, torch, src, dst, ratio):
         wbytes = dst.numel() * dst.element_size()
         assert src.numel() * src.element_size() >= ratio * wbytes
-        self.lib.probe_stream_mix.restype = ctypes.c_int
-        self.lib.probe_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_longlong, ctypes.c_int]
         rc = self.lib.probe_stream_mix(torch.cuda.current_stream().cuda_stream, src.data_ptr(),
                                        dst.data_ptr(), wbytes, ratio)
         if rc != 0:
