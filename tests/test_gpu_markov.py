@@ -125,6 +125,18 @@ def test_markov_smallest_vocabulary():
     assert parted <= partings_bound(compared)
 
 
+def test_markov_single_request_single_position():
+    """R = 1, gamma = 1: one bias launch whose only row block holds one
+    request, one select, one confidence; and the full rank (256)."""
+    inp = markov_inputs(R=1, gamma=1, V=3000, rank=256, H=8, rank_e=8, sigma_u=1.0, sigma_f=0.1, seed=93,
+                        device="cuda")
+    out = _run(inp)
+    assert np.all(to_np(out["status"]) == 0)
+    ref = oracle_chain(inp, range(1), keep=range(1))
+    compared, parted, _ = check_chain(inp, out, ref, range(1))
+    assert parted <= partings_bound(compared)
+
+
 @pytest.mark.parametrize("rank", [96, 160, 224])
 def test_markov_ranks_off_the_powers_of_two(rank):
     """rank = 32 * 3, 5, 7: C rows of 12, 20, 28 sixteen-byte chunks (the LDS

@@ -116,6 +116,16 @@ def test_rnn_smallest_vocabulary():
     assert parted <= partings_bound(compared)
 
 
+def test_rnn_single_request_single_position():
+    """R = 1, gamma = 1: the state is initialised and never advanced."""
+    inp = rnn_inputs(R=1, gamma=1, V=3000, d=64, H=8, rank_e=8, sigma_c=0.3, seed=97, device="cuda")
+    out = _run(inp)
+    assert np.all(to_np(out["status"]) == 0)
+    ref = oracle_chain(inp, range(1), keep=range(1))
+    compared, parted, _ = check_chain(inp, out, ref, range(1))
+    assert parted <= partings_bound(compared)
+
+
 @pytest.mark.parametrize("d", [32, 96, 128])
 def test_rnn_state_sizes_and_positions(d):
     inp = rnn_inputs(R=9, gamma=6, V=1000, d=d, H=16, rank_e=8, sigma_c=0.4, seed=96 + d, device="cuda")
