@@ -842,6 +842,13 @@ size_t verify_ws_bytes(int R, int gmax, int V) {
 // for the requests that accepted every position so far.
 int next_cover(int cover) { return 2 * cover + 2; }
 
+// Full-pass items (request x slot x chunk) from which a bf16 pass takes two
+// chunks per workgroup.
+#ifndef SDV_PAIRED_PASS_MIN_ITEMS
+#define SDV_PAIRED_PASS_MIN_ITEMS 16384
+#endif
+constexpr long long kPairedPassMinItems = SDV_PAIRED_PASS_MIN_ITEMS;
+
 // Draws spread over the chip: at most this many requests (measured: the two
 // extra launches cost more than they save once the requests fill the CUs),
 // and rows of at least this many residual blocks (measured, graph-replayed
@@ -934,6 +941,10 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   ra.list = nullptr;
   ra.count = nullptr;
   ra.clear = nullptr;
+  // Two chunks of a bf16 row per workgroup once the full pass has many items
+  // (measured at the headline size: 249 against 258 us per pass; with the
+  // 2176 items of R = 64, gamma = 8, V = 32000, two chunks were slower).
+  ra.chunks = (dtype == SD_DTYPE_BF16 && items >= kPairedPassMinItems) ? 2 : 1;
   // target slots [t_lo, t_hi) and draft positions [d_lo, d_hi] of one pass
   auto set_range = [&](int t_lo, int t_hi, int d_lo, int d_hi) {
     if (drf_stats) d_hi = d_lo - 1;  // the drafter's statistics replace the draft rows
@@ -991,7 +1002,8 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
   if (!lazy) {  // every row of the batch in one pass
     set_range(0, gamma_max + 1, 1, gamma_max);
     if (prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
-    SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, (unsigned)((long long)R * ra.slots * n_ch), stream));
+    SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, (unsigned)((long long)R * ra.slots * sdv::pass_groups(n_ch, ra.chunks)),
+                                            stream));
     if (prof_stop) SDV_TRY_LAUNCH(hipEventRecord(prof_stop, stream));
     return bf16 ? launch_finish<true, kFused>(stream, R, a) : launch_finish<false, kFused>(stream, R, a);
   }
@@ -1009,7 +1021,7 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
     ra.list = k ? lists + (size_t)k * R : nullptr;
     ra.count = k ? counts + k : nullptr;
     ra.clear = last ? nullptr : counts + k + 1;
-    const long long n_items = (long long)R * ra.slots * n_ch;
+    const long long n_items = (long long)R * ra.slots * sdv::pass_groups(n_ch, ra.chunks);
     const unsigned grid = k ? (unsigned)std::min<long long>(n_items, kListGrid) : (unsigned)n_items;
     if (k == 0 && prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
     if (grid > 0) SDV_TRY_LAUNCH(sdv::launch_row_partials(bf16, ra, grid, stream));

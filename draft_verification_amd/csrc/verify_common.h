@@ -9,7 +9,10 @@ namespace sdv {
 
 constexpr int kRowThreads = 256;                   // bandwidth-pass workgroup
 constexpr int kRowWaves = kRowThreads / 64;        // partials per (row, chunk)
-constexpr int kChunk = 16384;                      // elements per bandwidth-pass item
+constexpr int kChunk = 16384;                      // elements per chunk of a row
+// Chunks of one row per bandwidth-pass workgroup (1 or 2), all their loads
+// issued together: the items of a pass are (request, slot, chunk group).
+__host__ __device__ inline int pass_groups(int n_ch, int chunks) { return (n_ch + chunks - 1) / chunks; }
 constexpr int kMaxChunks = SD_MAX_VOCAB / kChunk;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -75,9 +78,10 @@ struct RowPassArgs {
   const int32_t* list;   // the requests of this pass (null: every request) ...
   const int32_t* count;  // ... and their number
   int32_t* clear;        // counter the next round appends to, zeroed here (or null)
+  int chunks;            // consecutive chunks per workgroup: 1, or 2 (bf16 only)
 };
 
-// Launch the bandwidth pass: one workgroup per (request, slot, chunk) item
+// Launch the bandwidth pass: one workgroup per (request, slot, chunk group) item
 // without a list, else `grid` workgroups striding over the listed items.
 hipError_t launch_row_partials(bool bf16, const RowPassArgs& a, unsigned grid, hipStream_t stream);
 
