@@ -1,9 +1,11 @@
 // libsdv_probe: the benchmark's measurement aid, built beside libsdv and not
-// part of its interface.  A plain streaming read with the same load shape as
-// the bandwidth pass of sd_verify on a large bf16 batch (256-thread
-// workgroups, sixteen 16-byte non-temporal loads per thread, 64 KB per
-// workgroup); its duration over a buffer of the batch's size is the
-// practical HBM read ceiling that the bandwidth pass is compared with.
+// part of its interface.  A plain streaming read: 256-thread workgroups,
+// each thread issuing 32 16-byte non-temporal loads together (128 KB per
+// workgroup), folded to one word per workgroup.  Of the plain reads measured
+// (32, 64 and 128 KB per workgroup, with and without a pause between two
+// halves) this shape was the fastest, 7.0 against 6.7-6.8 TB/s over 1.79 GB;
+// its duration over a buffer of the batch's size is the practical HBM read
+// ceiling that the bandwidth pass is compared with.
 //
 //   long long probe_stream_read_sink_words(long long bytes)
 //       uint32 words the sink needs for `bytes` (-1 for bytes < 0)
@@ -24,7 +26,7 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPer = 16;
+constexpr int kPer = 32;
 constexpr long long kVecPerBlock = (long long)kThreads * kPer;
 
 __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* __restrict__ src, long long n,

@@ -154,9 +154,10 @@ def test_read_probe_is_outside_the_library():
     P.probe_stream_read_sink_words.restype = ctypes.c_longlong
     P.probe_stream_read_sink_words.argtypes = [ctypes.c_longlong]
     P.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
-    assert P.probe_stream_read_sink_words(0) == 0
-    assert P.probe_stream_read_sink_words(32768) == 1
-    assert P.probe_stream_read_sink_words(32784) == 2
+    assert P.probe_stream_read_sink_words(0) == 0              # one word per 128 KB workgroup
+    assert P.probe_stream_read_sink_words(16) == 1
+    assert P.probe_stream_read_sink_words(131072) == 1
+    assert P.probe_stream_read_sink_words(131088) == 2
     assert P.probe_stream_read_sink_words(-16) == -1
     p = ctypes.c_void_p(256)
     assert P.probe_stream_read(None, p, 24, p) == _lib.SD_EINVAL        # not a multiple of 16
