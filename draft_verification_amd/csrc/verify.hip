@@ -1021,6 +1021,8 @@ extern "C" int sd_verify(hipStream_t stream, int R, int gamma_max, int V, int ld
     ra.list = k ? lists + (size_t)k * R : nullptr;
     ra.count = k ? counts + k : nullptr;
     ra.clear = last ? nullptr : counts + k + 1;
+    // the listed rounds cover a fraction of the requests: one chunk each
+    ra.chunks = (bf16 && k == 0 && (long long)R * ra.slots * n_ch >= kPairedPassMinItems) ? 2 : 1;
     const long long n_items = (long long)R * ra.slots * sdv::pass_groups(n_ch, ra.chunks);
     const unsigned grid = k ? (unsigned)std::min<long long>(n_items, kListGrid) : (unsigned)n_items;
     if (k == 0 && prof_start) SDV_TRY_LAUNCH(hipEventRecord(prof_start, stream));
