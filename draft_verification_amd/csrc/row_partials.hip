@@ -86,11 +86,15 @@ __device__ __forceinline__ void row_chunks(const sdv::RowPassArgs& a, int r, int
     }
   }
   chunk_partial<BF16>(a, buf[0], rs, ch0);
-  // The next chunk's reduction waits until this partial is stored (all of
-  // the wave's loads are in by now).  Measured at the headline size: 249 us
-  // per pass with the wait, 257 us without (the ragged step's pass: 417
-  // against 402 us).
-  if (kPassChunks > 1) __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  // Where the request's whole reserved block is in the batch, the next
+  // chunk's reduction waits until this partial is stored (all of the wave's
+  // loads are in by now): with every workgroup streaming, the pass runs
+  // faster with that pause, which holds back new loads (measured: 249 us per
+  // headline pass with it, 257 us without).  Where slots of the block are
+  // outside the batch, their workgroups exit at once and the pass wants
+  // every load in flight it can get (ragged step: 403 us without the pause
+  // there, 416 us with it).
+  if (kPassChunks > 1 && L == a.gmax) __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
 #pragma unroll
   for (int h = 1; h < kPassChunks; ++h)
     if (ch0 + h < a.n_ch) chunk_partial<BF16>(a, buf[h], rs, ch0 + h);
