@@ -126,6 +126,23 @@ def test_verify_vocab_past_the_lds_block_sums():
         _full_check(inp, np.full(R, g))
 
 
+def test_verify_paired_chunks_odd_count_and_ragged_lengths():
+    """A bf16 batch large enough for two chunks per bandwidth-pass workgroup
+    (R * (2 gamma_max + 1) * chunks >= 16384) with an odd number of chunks
+    per row (V = 33576: three chunks, the last pair holding one), and lengths
+    from 0 to gamma_max (requests whose whole block is scheduled, and
+    requests with slots outside it); sampled requests of every length."""
+    R, g, V = 160, 20, 33576
+    inp = _to_cuda(verify_inputs(R=R, gmax=g, V=V, dtype=torch.bfloat16, sigma_t=2.0, zipf=True,
+                                 sigma_d=(0.5, 2.5), seed=88))
+    rng = np.random.default_rng(88)
+    ell = rng.integers(0, g + 1, R)
+    ell[:8] = g
+    reqs = sorted(set([int(i) for i in range(8)] + [int(np.flatnonzero(ell == L)[0]) for L in np.unique(ell)]))
+    _, ora = _full_check(inp, ell, reqs=reqs)
+    _lazy_check(inp, ell, reqs=reqs, ora=ora)
+
+
 def test_verify_draws_in_the_request_workgroup():
     """Batches of more than 128 requests make each correction draw inside the
     request's own finishing workgroup (smaller batches of rows of 64 or more
